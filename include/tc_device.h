@@ -1,0 +1,120 @@
+/*
+ * tc_device.h -- device view of a triggered plan, for HIP kernels on gfx950.
+ *
+ * Producer side ([TP] = "Triggered Plans", section Memory ordering): a chunk's
+ * data must be in memory before its gate opens.  Every wave waits for its own
+ * stores (s_waitcnt vmcnt(0)), the CTA barrier makes that true for every wave,
+ * then one thread adds 1 to the chunk's writer counter with a release at
+ * system scope (which writes back this XCD's L2); the writer whose increment
+ * completes the round's count then stores the round into `ready`.  The gate
+ * store itself needs no release: it follows the releasing increment.
+ *
+ * Consumer side (same section; [TP] The kernel author's contract, item 5):
+ * arrived/wait read the arrival counter with an acquire at system scope.  One
+ * thread reads, the CTA barrier hands the result to every wave, and polling
+ * loops count polls instead of reading a clock, so every wave takes the same
+ * exit.  All tc_mark_ready / tc_arrived / tc_wait calls are whole-CTA calls:
+ * every thread of the CTA must make them, outside divergent branches.
+ *
+ * Gate rows: rank src's chunk c has global id chunk_base[src] + c; its row in
+ * rank q's table is at gates + q * gate_stride + id * 64.  `ready` and the
+ * writer counter live in the sender's own table (q == src), `arrival` in
+ * each receiver's table.  A rank's own chunk never "arrives" at itself:
+ * tc_arrived(dst == src) means its gate is open.
+ */
+#ifndef TC_DEVICE_H
+#define TC_DEVICE_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tc.h"
+
+/* s_waitcnt with vmcnt = 0 and expcnt / lgkmcnt left at their maxima (gfx9
+ * encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+ * On gfx9 stores are counted by vmcnt, so this waits for the wave's stores,
+ * buffer stores included. */
+#define TC_WAITCNT_VMCNT0 0x0F70
+
+__device__ inline tc_gate_row* tc_gate_row_ptr(const tc_handle& h, uint32_t table_rank,
+                                               uint32_t src, uint32_t chunk) {
+  return reinterpret_cast<tc_gate_row*>(h.gates + (uint64_t)table_rank * h.gate_stride +
+                                        (uint64_t)(h.chunk_base[src] + chunk) * TC_GATE_ROW_BYTES);
+}
+
+__device__ inline bool tc_is_cta_leader() {
+  return threadIdx.x == 0 && threadIdx.y == 0 && threadIdx.z == 0;
+}
+
+/* mark_ready(chunk) by one writer CTA of rank `rank`.  Whole CTA. */
+__device__ inline void tc_mark_ready(const tc_handle& h, uint32_t rank, uint32_t chunk) {
+  __builtin_amdgcn_s_waitcnt(TC_WAITCNT_VMCNT0);  // this wave's stores are done
+  __syncthreads();                                // ... and so are every other wave's
+  if (tc_is_cta_leader()) {
+    tc_gate_row* row = tc_gate_row_ptr(h, rank, rank, chunk);
+    const uint32_t* writers = reinterpret_cast<const uint32_t*>(h.writers);
+    const uint64_t w = writers[h.chunk_base[rank] + chunk];
+    const uint64_t old = __hip_atomic_fetch_add(&row->writers, (uint64_t)1, __ATOMIC_RELEASE,
+                                                __HIP_MEMORY_SCOPE_SYSTEM);
+    if (old + 1 == (uint64_t)h.round * w)          // the last writer of this round
+      __hip_atomic_store(&row->ready, (uint64_t)h.round, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+  __syncthreads();
+}
+
+/* One acquire poll of chunk (src, chunk) as seen by rank dst.  Leader only. */
+__device__ inline bool tc_poll_once(const tc_handle& h, uint32_t dst, uint32_t src,
+                                    uint32_t chunk) {
+  tc_gate_row* row = tc_gate_row_ptr(h, dst, src, chunk);
+  const uint64_t* field = (dst == src) ? &row->ready : &row->arrival;
+  const uint32_t lo = (uint32_t)__hip_atomic_load(field, __ATOMIC_ACQUIRE,
+                                                  __HIP_MEMORY_SCOPE_SYSTEM);
+  return lo >= h.round;
+}
+
+/* arrived(chunk): has rank src's chunk of this round arrived at rank dst?
+ * One atomic; the result reaches every wave through the CTA barrier. */
+__device__ inline bool tc_arrived(const tc_handle& h, uint32_t dst, uint32_t src, uint32_t chunk) {
+  __shared__ uint32_t tc_flag;
+  if (tc_is_cta_leader()) tc_flag = tc_poll_once(h, dst, src, chunk) ? 1u : 0u;
+  __syncthreads();
+  const bool ok = tc_flag != 0;
+  __syncthreads();
+  return ok;
+}
+
+/* wait(chunk) with at most max_polls polls (counted, never timed); returns
+ * whether the chunk arrived.  Data read after a true return is this round's. */
+__device__ inline bool tc_wait(const tc_handle& h, uint32_t dst, uint32_t src, uint32_t chunk,
+                               uint32_t max_polls) {
+  __shared__ uint32_t tc_flag;
+  if (tc_is_cta_leader()) {
+    uint32_t ok = 0;
+    for (uint32_t i = 0; i < max_polls; ++i) {
+      if (tc_poll_once(h, dst, src, chunk)) { ok = 1; break; }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    tc_flag = ok;
+  }
+  __syncthreads();
+  const bool ok = tc_flag != 0;
+  __syncthreads();
+  return ok;
+}
+
+/* The producer's step->tile map: group_m tile-rows walked column by column,
+ * then the next band of rows (the grouped order [TP] Model's tile_of stands
+ * for).  Plain integer arithmetic, shared by host and device so the schedule
+ * and the kernel cannot drift. */
+__host__ __device__ inline uint32_t tc_tile_of(uint32_t step, uint32_t tm, uint32_t tn,
+                                               uint32_t group_m) {
+  const uint32_t width = group_m * tn;
+  const uint32_t first_m = (step / width) * group_m;
+  const uint32_t left = tm - first_m;
+  const uint32_t size_m = left < group_m ? left : group_m;
+  const uint32_t in_band = step % width;
+  return (first_m + in_band % size_m) * tn + in_band / size_m;
+}
+
+#endif /* TC_DEVICE_H */

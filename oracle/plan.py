@@ -63,16 +63,23 @@ def copy_region(dst: np.ndarray, src: np.ndarray, reg) -> None:
 
 
 class PlanSim:
-    """P replicas (uint8 numpy arrays of equal size), one schedule per rank."""
+    """P replicas (uint8 numpy arrays of equal size), one schedule per rank.
 
-    def __init__(self, replicas: List[np.ndarray], schedules: Sequence[Optional[Schedule]],
-                 own_rows_bytes: Optional[int] = None):
-        self.P = len(replicas)
+    With ``replicas=None`` (and ``buffer_bytes`` given) only gates, cursors
+    and delivery logs are simulated: the copies are skipped, which changes no
+    counter (counters never depend on the bytes copied)."""
+
+    def __init__(self, replicas: Optional[List[np.ndarray]], schedules: Sequence[Optional[Schedule]],
+                 own_rows_bytes: Optional[int] = None, buffer_bytes: Optional[int] = None):
+        self.P = len(replicas) if replicas is not None else len(schedules)
         if self.P == 0 or len(schedules) != self.P:
             raise PlanError("EINVAL", "one schedule per rank")
-        size = replicas[0].size
-        if any(r.size != size for r in replicas):
-            raise PlanError("EINVAL", "replicas differ in size")
+        if replicas is None:
+            size = buffer_bytes
+        else:
+            size = replicas[0].size
+            if any(r.size != size for r in replicas):
+                raise PlanError("EINVAL", "replicas differ in size")
         try:
             validate(size, schedules, own_rows_bytes)
         except ScheduleError as e:
@@ -125,8 +132,9 @@ class PlanSim:
         c = int(self.cur[p, q])
         if c >= self.n[p] or not self.gate_open(p, c):
             return False
-        for reg in self.sched[p].chunks[c].regions:
-            copy_region(self.rep[q], self.rep[p], reg)
+        if self.rep is not None:
+            for reg in self.sched[p].chunks[c].regions:
+                copy_region(self.rep[q], self.rep[p], reg)
         self.gates[q, self.g(p, c), ARRIVAL] += np.uint64(1)
         self.cur[p, q] = c + 1
         self.log[(p, q)].append(c)

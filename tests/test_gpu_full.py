@@ -1,0 +1,229 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark uses.
+
+* GEMM producer: within rtol 1e-2 of the fp32 CPU reference; replicas,
+  gates and cursors bit-exact against the oracle fed each rank's GPU block.
+* 8 ranks x 4 MiB whole chunk, 8 writers, 10 rounds; the extra-mark run.
+* 4 ranks x 1.5 GiB (chunks of 0.5 GiB; one whole chunk cut at 1 GiB):
+  replicas compared with each other in full and with the oracle's values on
+  sampled elements (chunk and region edges included); gates and cursors
+  bit-exact against the counters-only oracle.
+* 8 ranks of 2-D tiles completed in a shuffled order, stepped one chunk at a
+  time: after every step the gates equal the oracle's (head-of-line order).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import triggered_copy_amd as tc
+from oracle import gemm as ogemm
+from oracle import plan as oplan
+from oracle import values as ovalues
+from synth import BASE_SEED, gemm_operands, workloads
+from tests.gpu_common import Pair, log, oracle_produce, require_gpu, wait_until
+
+pytestmark = pytest.mark.gpu
+
+
+def _u16_to_dev(a):
+    return torch.from_numpy(a.view(np.int16)).cuda()
+
+
+@pytest.mark.parametrize("M,N,K,programs,group_m", [(300, 264, 128, 7, 2), (2000, 2000, 1024, 256, 8),
+                                                    (128, 128, 64, 1, 1), (1, 8, 8, 3, 8)])
+def test_gemm_matches_reference(M, N, K, programs, group_m):
+    require_gpu()
+    log(f"gemm {M}x{N}x{K} programs={programs}")
+    a, bt = gemm_operands(BASE_SEED, 0, 1, M, N, K)
+    C_out = torch.zeros((M, N), dtype=torch.int16, device="cuda")
+    tc.gemm_bf16(_u16_to_dev(a), _u16_to_dev(bt), C_out, programs=programs, group_m=group_m)
+    torch.cuda.synchronize()
+    got = ogemm.bf16_bits_to_f32(C_out.cpu().numpy().view(np.uint16))
+    ok, worst, frob = ogemm.within_tolerance(got, ogemm.gemm_ref(a, bt), 1e-2)
+    assert ok, (worst, frob)
+
+
+def test_gemm_tiles_p4_full():
+    w = workloads.FULL["gemm_tiles_p4"]
+    pair = Pair(w)
+    P, M, N, K = w["P"], w["rows"], w["cols"], w["K"]
+    try:
+        for r in range(1, w["rounds"] + 1):
+            log(f"gemm_tiles_p4 round {r}")
+            ops = [gemm_operands(BASE_SEED, p, r, M, N, K) for p in range(P)]
+            dev = [(_u16_to_dev(a), _u16_to_dev(bt)) for a, bt in ops]
+            torch.cuda.synchronize()
+            h = pair.plan.start(pair.stream)
+            for p in range(P):
+                C_out = pair.rep[p][p * M * N * 2:]
+                tc.gemm_bf16(dev[p][0], dev[p][1], C_out, ldc=N, M=M, N=N, programs=w["programs"],
+                             group_m=w["group_m"], handle=h, rank=p, first_chunk=0,
+                             tiles_per_chunk=w["tiles_per_chunk"], stream=pair.stream)
+            pair.plan.wait(20.0)
+            torch.cuda.synchronize()
+            host = pair.rep.cpu().numpy()
+            blocks = []
+            for p in range(P):
+                blk = host[p][p * M * N * 2:(p + 1) * M * N * 2]
+                got = ogemm.bf16_bits_to_f32(blk.view(np.uint16).reshape(M, N))
+                ok, worst, frob = ogemm.within_tolerance(got, ogemm.gemm_ref(*ops[p]), 1e-2)
+                assert ok, (p, worst, frob)
+                blocks.append(blk.copy())
+
+            def produce(p, rr):   # the oracle is fed each rank's GPU block
+                pair.sim.rep[p][p * M * N * 2:(p + 1) * M * N * 2] = blocks[p]
+            oplan.run_round(pair.sim, produce)
+            pair.compare(f"gemm_tiles_p4 round {r}")
+            pair.plan.next_round()
+            pair.sim.next_round()
+    finally:
+        pair.close()
+
+
+def test_u32_whole_p8_ten_rounds():
+    w = workloads.FULL["u32_whole_p8"]
+    pair = Pair(w)
+    try:
+        for r in range(1, w["rounds"] + 1):
+            log(f"u32_whole_p8 round {r}")
+            pair.gpu_round_fill()
+            pair.oracle_round()
+            pair.compare(f"u32_whole_p8 round {r}")
+            if r < w["rounds"]:
+                pair.plan.next_round()
+                pair.sim.next_round()
+        g = pair.plan.gates().view(np.uint64).reshape(w["P"], -1, 8)
+        for p in range(w["P"]):
+            assert (int(g[p, p, 2]), int(g[p, p, 0])) == (80, 10)
+            assert all(int(g[q, p, 1]) == 10 for q in range(w["P"]) if q != p)
+    finally:
+        pair.close()
+
+
+def test_u32_whole_p8_extra_mark_round7():
+    w = workloads.FULL["u32_whole_p8"]
+    pair = Pair(w)
+    er, rank = w["extra_round"], w["extra_rank"]
+    try:
+        for r in range(1, er + 1):
+            log(f"u32_whole_p8 extra-mark run round {r}")
+            h = pair.plan.start(pair.stream)
+            pair.plan.fill(h, pair.tv, pair.seed, kind="u32", stream=pair.stream)
+            if r < er:
+                pair.plan.wait(10.0)
+                pair.oracle_round()
+                pair.compare(f"extra-mark run round {r}")
+                pair.plan.next_round()
+                pair.sim.next_round()
+                continue
+            pair.plan.mark(h, rank, 0, 1, stream=pair.stream)
+            with pytest.raises(tc.ExtraMarksError) as ei:
+                pair.plan.wait(10.0)
+            with pytest.raises(oplan.PlanError) as eo:
+                pair.oracle_round(extra=[(rank, 0)])
+            assert ei.value.chunks == eo.value.chunks == [(rank, 0)]
+            assert pair.plan.state == "FAILED"
+            torch.cuda.synchronize()
+            assert np.array_equal(pair.plan.gates(), pair.sim.gate_bytes())
+            g = pair.plan.gates().view(np.uint64).reshape(w["P"], -1, 8)
+            assert int(g[rank, rank, 2]) == 8 * er + 1
+    finally:
+        pair.close()
+
+
+def _sample_check(pair, w, r, rng, nsamp=1 << 18):
+    """Replicas equal each other in full; sampled elements equal the oracle's
+    values (chunk and region edges always included)."""
+    P, rows, cols = w["P"], w["rows"], w["cols"]
+    n = rows * cols
+    for q in range(1, P):
+        assert torch.equal(pair.rep[0], pair.rep[q]), f"replica {q} differs from replica 0"
+    edges = set()
+    for s in pair.os:
+        for ch in s.chunks:
+            for off, rr, rb, pitch in ch.regions:
+                for b in (off, off + rb - 4):
+                    edges.add(b)
+    for p in range(P):
+        base = p * n * 4
+        idx = rng.integers(0, n, size=nsamp, dtype=np.int64)
+        extra = [(e - base) // 4 for e in edges if base <= e < base + n * 4]
+        idx = np.unique(np.concatenate([idx, np.array(extra, dtype=np.int64), [0, n - 1]]))
+        q = int(rng.integers(0, P))
+        words = pair.rep[q].view(torch.int32)[p * n:(p + 1) * n]
+        got = words[torch.from_numpy(idx).cuda()].cpu().numpy().view(np.uint32)
+        want = ovalues.u32_pattern(pair.seed, p, r, idx.astype(np.uint64))
+        bad = np.flatnonzero(got != want)
+        assert bad.size == 0, f"rank {p} in replica {q}: {bad.size} sampled elements differ, e.g. index {idx[bad[:4]]}"
+
+
+@pytest.mark.parametrize("name", ["u32_chunks_1p5g_p4", "u32_whole_1p5g_p4"])
+def test_u32_1p5g_p4_full(name):
+    w = workloads.FULL[name]
+    rng = np.random.default_rng(5)
+    pair = Pair(w, oracle_bytes=False)
+    try:
+        for r in range(1, w["rounds"] + 1):
+            deferred = r == 2
+            log(f"{name} round {r} ({'deferred' if deferred else 'in-kernel'} marks)")
+            pair.gpu_round_fill(mark=not deferred, timeout=30.0)
+            pair.oracle_round()
+            pair.compare(f"{name} round {r}")
+            _sample_check(pair, w, r, rng)
+            pair.plan.next_round()
+            pair.sim.next_round()
+    finally:
+        pair.close()
+
+
+def test_u32_tiles_shuffled_p8_rounds():
+    w = workloads.FULL["u32_tiles_shuffled_p8"]
+    pair = Pair(w)
+    try:
+        for r in range(1, w["rounds"] + 1):
+            log(f"u32_tiles_shuffled_p8 round {r}")
+            orders, dev = pair.orders_device(r)
+            pair.gpu_round_fill(serial=True, order=dev, order_stride=orders.shape[1])
+            mark_order = [(p, int(c)) for p in range(pair.P) for c in orders[p]
+                          for _ in range(pair.sim.writers(p, int(c)))]
+            pair.oracle_round(mark_order=mark_order)
+            pair.compare(f"shuffled round {r}")
+            pair.plan.next_round()
+            pair.sim.next_round()
+    finally:
+        pair.close()
+
+
+def test_head_of_line_stepped_p8():
+    w = workloads.FULL["u32_tiles_shuffled_p8"]
+    pair = Pair(w)
+    try:
+        for r in (1, 2):
+            orders, _ = pair.orders_device(r)
+            h = pair.plan.start(pair.stream)
+            pair.plan.fill(h, pair.tv, pair.seed, kind="u32", mark=False, stream=pair.stream)
+            pair.sim.start()
+            for p in range(pair.P):
+                oracle_produce(pair.sim.rep[p], pair.ov[p], "u32", pair.seed, p, r)
+            n = orders.shape[1]
+            for k in range(n):
+                for p in range(pair.P):
+                    c = int(orders[p][k])
+                    wr = pair.sim.writers(p, c)
+                    pair.plan.mark(h, p, c, wr, stream=pair.stream)
+                    for _ in range(wr):
+                        pair.sim.mark(p, c)
+                    want_g = pair.sim.gate_bytes()
+                    ok = wait_until(lambda: np.array_equal(pair.plan.cursors(), pair.sim.cur)
+                                    and np.array_equal(pair.plan.gates(), want_g), 5.0)
+                    assert ok, f"round {r} step ({p},{c}): cursors {pair.plan.cursors()[p].tolist()} " \
+                               f"vs oracle {pair.sim.cur[p].tolist()}"
+            log(f"head-of-line round {r}: {n * pair.P} steps matched")
+            pair.plan.wait(10.0)
+            pair.sim.wait()
+            pair.compare(f"stepped round {r}")
+            pair.plan.next_round()
+            pair.sim.next_round()
+    finally:
+        pair.close()

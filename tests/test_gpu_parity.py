@@ -1,0 +1,287 @@
+"""GPU parity: the HIP path against the CPU oracle, element by element.
+
+Bit-exact replicas, gate tables and queue cursors after every round, on the
+small workloads (several tiles, ragged tails, unaligned pitches) and on the
+two-rank bf16 workload at its full size; the barrier against its closed form
+and reveal; the misuse paths (extra mark, withheld mark, round limit, state
+order).  Every call goes through the C boundary.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import triggered_copy_amd as tc
+from oracle import barrier as obarrier
+from oracle import plan as oplan
+from synth import workloads
+from tests.gpu_common import Pair, log, require_gpu, wait_until
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_all_rounds(name, w):
+    pair = Pair(w)
+    try:
+        for r in range(1, w["rounds"] + 1):
+            log(f"{name} round {r}")
+            if w.get("shuffled"):
+                orders, dev = pair.orders_device(r)
+                pair.gpu_round_fill(serial=True, order=dev, order_stride=orders.shape[1])
+                mark_order = [(p, int(c)) for p in range(pair.P) for c in orders[p]
+                              for _ in range(pair.sim.writers(p, int(c)))]
+                pair.oracle_round(mark_order=mark_order)
+            else:
+                pair.gpu_round_fill()
+                pair.oracle_round()
+            pair.compare(f"{name} round {r}")
+            assert pair.plan.state == "DONE"
+            pair.plan.next_round()
+            pair.sim.next_round()
+    finally:
+        pair.close()
+
+
+@pytest.mark.parametrize("name", sorted(workloads.SMALL))
+def test_small_workload_rounds(name):
+    _run_all_rounds(name, workloads.SMALL[name])
+
+
+def test_bf16_chunks_p2_full():
+    _run_all_rounds("bf16_chunks_p2", workloads.FULL["bf16_chunks_p2"])
+
+
+def test_deferred_marks_and_ctas_sweep():
+    w = dict(workloads.SMALL["u32_chunks_ragged_p3"])
+    for ctas, piece in ((1, 256), (3, 512), (64, 0)):
+        pair = Pair(w, engine_ctas=ctas, piece_bytes=piece)
+        try:
+            for r in (1, 2):
+                log(f"deferred ctas={ctas} piece={piece} round {r}")
+                pair.gpu_round_fill(mark=False)
+                pair.oracle_round()
+                pair.compare(f"deferred ctas={ctas} round {r}")
+                pair.plan.next_round()
+                pair.sim.next_round()
+        finally:
+            pair.close()
+
+
+def test_rank_that_sends_nothing_and_single_rank():
+    w = dict(P=3, rows=20, cols=24, elem="u32", builder="chunks", n=2, writers=1, rounds=2)
+    pair = Pair(w)
+    try:
+        pair.plan.close()
+        sched = list(pair.ts)
+        sched[1] = None                                   # broadcast-style: rank 1 silent
+        pair.plan = tc.TriggeredPlan(pair.rep, sched, backstop_s=20.0)
+        pair.sim = oplan.PlanSim(pair.sim.rep, [pair.os[0], None, pair.os[2]])
+        h = pair.plan.start(pair.stream)
+        pair.plan.fill(h, pair.tv, pair.seed, kind="u32", stream=pair.stream)
+        pair.plan.wait(10.0)
+
+        def produce(p, r):
+            if p != 1:
+                from tests.gpu_common import oracle_produce
+                oracle_produce(pair.sim.rep[p], pair.ov[p], "u32", pair.seed, p, r)
+        oplan.run_round(pair.sim, produce)
+        # the GPU fill writes only scheduled bytes, so rank 1's rows keep the sentinel
+        pair.compare("silent rank")
+    finally:
+        pair.close()
+    w1 = dict(P=1, rows=8, cols=64, elem="u32", builder="whole", writers=2, rounds=2)
+    _run_all_rounds("single rank", w1)
+
+
+def test_withheld_mark_times_out_then_resumes():
+    w = dict(workloads.SMALL["u32_chunks_ragged_p3"])
+    pair = Pair(w)
+    try:
+        h = pair.plan.start(pair.stream)
+        pair.plan.fill(h, pair.tv, pair.seed, kind="u32", mark=False, stream=pair.stream)
+        # every mark except one of rank 1's chunk 2
+        for p in range(3):
+            for c in range(5):
+                n = 2 - (1 if (p, c) == (1, 2) else 0)
+                pair.plan.mark(h, p, c, n, stream=pair.stream)
+        with pytest.raises(tc.PlanTimeout) as ei:
+            pair.plan.wait(0.5)
+        assert (1, 2) in ei.value.chunks and (1, 3) in ei.value.chunks
+        assert pair.plan.state == "STARTED"
+        # the oracle names the same chunks
+        pair.sim.start()
+        from tests.gpu_common import oracle_produce
+        for p in range(3):
+            oracle_produce(pair.sim.rep[p], pair.ov[p], "u32", pair.seed, p, 1)
+        for p in range(3):
+            for c in range(5):
+                for _ in range(2 - (1 if (p, c) == (1, 2) else 0)):
+                    pair.sim.mark(p, c)
+        with pytest.raises(oplan.PlanError) as eo:
+            pair.sim.wait()
+        assert sorted(ei.value.chunks) == sorted(eo.value.chunks)
+        pair.compare("after timeout", partial=True)
+        pair.plan.mark(h, 1, 2, 1, stream=pair.stream)
+        pair.sim.mark(1, 2)
+        pair.plan.wait(10.0)
+        pair.sim.wait()
+        pair.compare("after resume")
+        assert pair.plan.stats()["launches"] == 2
+    finally:
+        pair.close()
+
+
+def test_extra_mark_fails_the_plan():
+    w = dict(workloads.SMALL["u32_whole_p5"])
+    pair = Pair(w)
+    try:
+        for r in (1, 2):
+            h = pair.plan.start(pair.stream)
+            pair.plan.fill(h, pair.tv, pair.seed, kind="u32", stream=pair.stream)
+            extra = [(3, 0)] if r == 2 else []
+            for p, c in extra:
+                pair.plan.mark(h, p, c, 1, stream=pair.stream)
+            if r == 2:
+                with pytest.raises(tc.ExtraMarksError) as ei:
+                    pair.plan.wait(10.0)
+                assert ei.value.chunks == [(3, 0)]
+                with pytest.raises(oplan.PlanError) as eo:
+                    pair.oracle_round(extra=extra)
+                assert eo.value.code == "EEXTRA" and eo.value.chunks == [(3, 0)]
+                assert pair.plan.state == "FAILED"
+                torch.cuda.synchronize()
+                g = pair.plan.gates()
+                assert np.array_equal(g, pair.sim.gate_bytes())
+                with pytest.raises(tc.StateError):
+                    pair.plan.next_round()
+            else:
+                pair.plan.wait(10.0)
+                pair.oracle_round()
+                pair.compare("extra-mark run round 1")
+                pair.plan.next_round()
+                pair.sim.next_round()
+    finally:
+        pair.close()
+
+
+def test_state_order_and_round_limit():
+    w = dict(P=2, rows=4, cols=64, elem="u32", builder="whole", writers=1, rounds=1)
+    pair = Pair(w)
+    try:
+        with pytest.raises(tc.InvalidArgument):          # the legacy default stream
+            pair.plan.start(torch.cuda.default_stream())
+        with pytest.raises(tc.StateError):
+            pair.plan.wait(1.0)
+        with pytest.raises(tc.StateError):
+            pair.plan.next_round()
+        h = pair.plan.start(pair.stream)
+        with pytest.raises(tc.StateError):
+            pair.plan.start(pair.stream)
+        pair.plan.fill(h, pair.tv, pair.seed, kind="u32", stream=pair.stream)
+        pair.plan.wait(10.0)
+        pair.plan.debug_set_round(0xFFFFFFFF)
+        with pytest.raises(tc.RoundLimitError):
+            pair.plan.next_round()
+    finally:
+        pair.close()
+
+
+def test_create_rejects_overlap_and_small_workspace():
+    require_gpu()
+    rep = torch.zeros((2, 4096), dtype=torch.uint8, device="cuda")
+    whole_out = tc.whole(tc.View(0, 2, 2048, 2048, 1, 0))
+    with pytest.raises(tc.OverlapError):
+        tc.TriggeredPlan(rep, [whole_out, whole_out])
+    mine = [tc.whole(tc.View(p * 2048, 1, 2048, 2048, 1, 0)) for p in range(2)]
+    with pytest.raises(tc.WorkspaceTooSmall):
+        tc.TriggeredPlan(rep, mine, workspace=torch.empty(256, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(tc.BoundsError):
+        tc.TriggeredPlan(rep, [mine[1], mine[0]], own_rows_bytes=2048)
+
+
+def test_barrier_p8_thousand_generations():
+    require_gpu()
+    w = workloads.FULL["barrier_p8"]
+    P, G = w["P"], w["gens"]
+    W = torch.zeros((P, P), dtype=torch.int32, device="cuda")
+    x = torch.zeros((2, P), dtype=torch.int32, device="cuda")
+    y = torch.zeros((G, P), dtype=torch.int32, device="cuda")
+    snap = torch.zeros((G, P, P), dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    log("barrier P=8 x 1000")
+    tc.barrier(W, P, 1, G, status, x=x, y=y, snap=snap)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert np.array_equal(W.cpu().numpy(), obarrier.run(P, G))
+    assert np.array_equal(y.cpu().numpy(), obarrier.reveal(P, 1, G))
+    s = snap.cpu().numpy().astype(np.int64)
+    for i in range(G):
+        g = i + 1
+        off = ~np.eye(P, dtype=bool)
+        rows = s[i]
+        assert (np.diagonal(rows) == 0).all()
+        assert np.isin(rows[off], [g, g + 1]).all()
+    # one more generation on the same window: first_gen continues the count
+    tc.barrier(W, P, G + 1, 1, status)
+    torch.cuda.synchronize()
+    assert np.array_equal(W.cpu().numpy(), obarrier.closed_form(P, G + 1))
+
+
+def test_barrier_one_generation_rows_p2():
+    require_gpu()
+    W = torch.zeros((2, 2), dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    tc.barrier(W, 2, 1, 1, status)
+    torch.cuda.synchronize()
+    assert W.cpu().numpy().tolist() == obarrier.run(2, 1).tolist() == [[0, 1], [1, 0]]
+
+
+def test_barrier_missing_peer_ends_with_status():
+    require_gpu()
+    # Generation 2 on a zero window whose peers never ran generation 1: every
+    # wait must run out of polls and the kernel must still end.
+    W = torch.zeros((3, 3), dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    tc.barrier(W, 3, 2, 1, status, max_polls=2000)
+    torch.cuda.synchronize()
+    assert int(status.item()) != 0
+
+
+def test_device_view_consumer_sees_fresh_data():
+    w = dict(workloads.SMALL["u32_tiles_shuffled_p3"])
+    pair = Pair(w)
+    try:
+        G = pair.plan.G
+        out = torch.full_like(pair.rep[0], 0x5A)
+        status = torch.zeros(G, dtype=torch.int32, device="cuda")
+        side = torch.cuda.Stream()
+        for r in (1, 2):
+            log(f"consumer round {r}")
+            status.zero_()
+            orders, dev = pair.orders_device(r)
+            torch.cuda.synchronize()         # nothing may wait for the device after start()
+            h = pair.plan.start(pair.stream)
+            # The consumer spins on arrivals, so it is queued after the work it
+            # depends on: streams may share a hardware queue.
+            pair.plan.fill(h, pair.tv, pair.seed, kind="u32", serial=True, order=dev,
+                           order_stride=orders.shape[1], stream=pair.stream)
+            with torch.cuda.stream(side):
+                pair.plan.consume_copy(h, 2, out, status, max_polls=1 << 22, stream=side)
+            pair.plan.wait(10.0)
+            side.synchronize()
+            pair.oracle_round()
+            pair.compare(f"consumer round {r}")
+            assert (status.cpu().numpy() == 1).all()
+            # what the consumer copied out of replica 2 is this round's data
+            got = out.cpu().numpy()
+            want = pair.sim.rep[2]
+            for s in pair.os:
+                for ch in s.chunks:
+                    for off, rows, rb, pitch in ch.regions:
+                        for i in range(rows):
+                            a = off + i * pitch
+                            assert np.array_equal(got[a:a + rb], want[a:a + rb])
+            pair.plan.next_round()
+            pair.sim.next_round()
+    finally:
+        pair.close()

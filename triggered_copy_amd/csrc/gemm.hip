@@ -1,0 +1,201 @@
+// Persistent bf16 GEMM producer with an in-kernel mark_ready.
+//
+// [TP] = "Triggered Plans" (Iris documentation), section Model: the example
+// producer is a persistent tiled kernel whose program p takes steps p,
+// p + programs, ...; each step computes the tile tile_of(step) picks, stores
+// it, then marks chunk first_chunk + step / tiles_per_chunk ready.  The host
+// builds the schedule with tile_chunks() from the same tile_of, so the two
+// cannot disagree.
+//
+// C[M,N] = A[M,K] * B, with B given as Bt[N,K] (K contiguous, so both
+// operands stream along K), bf16 inputs, fp32 accumulation on the matrix
+// cores, bf16 output (round to nearest even).
+//
+// gfx950 mapping: a 256-thread CTA computes a 128 x 128 tile; its 4 waves
+// form a 2 x 2 grid of 64 x 64 sub-tiles, each 4 x 4 blocks of the 16x16x32
+// bf16 MFMA (v_mfma_f32_16x16x32_bf16).  K advances 64 at a time: the next
+// A/B slab is fetched from global memory into registers while the current
+// one is multiplied out of LDS.  LDS rows are padded by 16 bytes to spread
+// the 16-byte fragment reads over the banks.  The finished tile is staged
+// through LDS so the bf16 stores are 16-byte vectors along the row.
+#include <hip/hip_runtime.h>
+
+#include <string>
+
+#include "internal.h"
+#include "plan_internal.h"
+#include "tc.h"
+#include "tc_device.h"
+
+using tc::fail;
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int LDA = BK + 8;            // bf16 elements per LDS row (144 bytes)
+constexpr int kThreads = 256;
+constexpr int LDC = BN + 8;            // bf16 elements per staged C row
+
+struct GemmArgs {
+  const uint16_t* A;
+  const uint16_t* Bt;
+  uint16_t* C;
+  uint64_t ldc;
+  uint32_t M, N, K;
+  uint32_t tm, tn, group_m;
+  uint32_t tiles;
+  uint32_t mark, rank, first_chunk, tiles_per_chunk;
+  tc_handle h;
+};
+
+__device__ inline uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
+  // One LDS area: A and B slabs during the K loop, the C tile afterwards.
+  constexpr int kSlab = BM * LDA;  // bf16 elements per operand slab
+  static_assert(2 * kSlab >= BM * LDC, "C staging fits in the operand area");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kSlab];
+  uint16_t* As = lds;
+  uint16_t* Bs = lds + kSlab;
+
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63, wave = tid >> 6;
+  const uint32_t wm = wave >> 1, wn = wave & 1;
+  const uint32_t nk = (a.K + BK - 1) / BK;
+
+  for (uint32_t step = blockIdx.x; step < a.tiles; step += gridDim.x) {
+    const uint32_t t = tc_tile_of(step, a.tm, a.tn, a.group_m);
+    const uint32_t m0 = (t / a.tn) * BM, n0 = (t % a.tn) * BN;
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Each thread moves 4 16-byte vectors of A and 4 of Bt per K slab:
+    // vector v = tid + 256 * s covers row v / 8, k columns 8 * (v % 8) .. +7.
+    u32x4 ra[4], rb[4];
+    auto fetch = [&](uint32_t kt) {
+      const uint32_t k0 = kt * BK;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t v = tid + kThreads * s;
+        const uint32_t r = v >> 3, kc = k0 + (v & 7) * 8;
+        const bool kin = kc < a.K;
+        ra[s] = (m0 + r < a.M && kin)
+                    ? *reinterpret_cast<const u32x4*>(a.A + (uint64_t)(m0 + r) * a.K + kc)
+                    : u32x4{0, 0, 0, 0};
+        rb[s] = (n0 + r < a.N && kin)
+                    ? *reinterpret_cast<const u32x4*>(a.Bt + (uint64_t)(n0 + r) * a.K + kc)
+                    : u32x4{0, 0, 0, 0};
+      }
+    };
+    fetch(0);
+    for (uint32_t kt = 0; kt < nk; ++kt) {
+      __syncthreads();  // the previous slab is no longer being read
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t v = tid + kThreads * s;
+        const uint32_t r = v >> 3, c = (v & 7) * 8;
+        *reinterpret_cast<u32x4*>(As + r * LDA + c) = ra[s];
+        *reinterpret_cast<u32x4*>(Bs + r * LDA + c) = rb[s];
+      }
+      __syncthreads();
+      if (kt + 1 < nk) fetch(kt + 1);  // in flight while this slab is multiplied
+#pragma unroll
+      for (int kk = 0; kk < BK; kk += 32) {
+        // Operand fragment of one 16x16x32 block: lane l holds row (l % 16)
+        // and 8 consecutive k values starting at 8 * (l / 16).
+        const uint32_t fr = lane & 15, fk = kk + 8 * (lane >> 4);
+        bf16x8 fa[4], fb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          fa[i] = *reinterpret_cast<const bf16x8*>(As + (wm * 64 + i * 16 + fr) * LDA + fk);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          fb[j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 64 + j * 16 + fr) * LDA + fk);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      }
+    }
+
+    // Stage the tile as bf16 in LDS.  Output block layout: lane l holds rows
+    // 4 * (l / 16) + e, e = 0..3, of column l % 16.
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t r = wm * 64 + i * 16 + 4 * (lane >> 4) + e;
+          const uint32_t c = wn * 64 + j * 16 + (lane & 15);
+          lds[r * LDC + c] = (uint16_t)f32_to_bf16_rne(acc[i][j][e]);
+        }
+    __syncthreads();
+    // 128 rows x 16 vectors of 8 bf16: 8 vectors per thread.
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint32_t v = tid + kThreads * s;
+      const uint32_t r = v >> 4, c = (v & 15) * 8;
+      if (m0 + r < a.M && n0 + c < a.N)
+        *reinterpret_cast<u32x4*>(a.C + (uint64_t)(m0 + r) * a.ldc + n0 + c) =
+            *reinterpret_cast<const u32x4*>(lds + r * LDC + c);
+    }
+    if (a.mark) tc_mark_ready(a.h, a.rank, a.first_chunk + step / a.tiles_per_chunk);
+  }
+}
+
+}  // namespace
+
+extern "C" int tc_gemm_bf16(const void* A, const void* Bt, void* C, uint32_t M, uint32_t N,
+                            uint32_t K, uint64_t ldc, uint32_t programs, uint32_t group_m,
+                            const tc_handle* h, uint32_t rank, uint32_t first_chunk,
+                            uint32_t tiles_per_chunk, void* stream) {
+  if (!A || !Bt || !C) return fail(TC_EINVAL, "gemm: NULL operand");
+  if (M == 0 || N == 0 || K == 0 || programs == 0 || group_m == 0)
+    return fail(TC_EINVAL, "gemm: zero size");
+  if (K % 8 || N % 8 || ldc % 8 || ldc < N)
+    return fail(TC_EINVAL, "gemm: K, N and ldc must be multiples of 8 (16-byte rows), ldc >= N");
+  if (((uintptr_t)A | (uintptr_t)Bt | (uintptr_t)C) & 15)
+    return fail(TC_EINVAL, "gemm: operands must be 16-byte aligned");
+  if (h && (tiles_per_chunk == 0 || rank >= h->nranks))
+    return fail(TC_EINVAL, "gemm: bad rank or tiles_per_chunk");
+  GemmArgs a{};
+  a.A = (const uint16_t*)A;
+  a.Bt = (const uint16_t*)Bt;
+  a.C = (uint16_t*)C;
+  a.ldc = ldc;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.tm = (M + BM - 1) / BM;
+  a.tn = (N + BN - 1) / BN;
+  a.group_m = group_m;
+  a.tiles = a.tm * a.tn;
+  if (h) {
+    a.mark = 1;
+    a.h = *h;
+    a.rank = rank;
+    a.first_chunk = first_chunk;
+    a.tiles_per_chunk = tiles_per_chunk;
+    const uint32_t nchunks = h->chunk_base[rank + 1] - h->chunk_base[rank];
+    if (first_chunk + (a.tiles - 1) / tiles_per_chunk >= nchunks)
+      return fail(TC_EINVAL, "gemm: the tiles map past the rank's chunks");
+  }
+  hipLaunchKernelGGL(gemm_kernel, dim3(programs), dim3(kThreads), 0, (hipStream_t)stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return tc::hip_fail(e, "gemm launch");
+  return TC_OK;
+}

@@ -1,0 +1,814 @@
+// Triggered plan runtime and its two kernels: the copy engine and the
+// completion check.
+//
+// [TP] = "Triggered Plans" (Iris documentation), [PR] = "Triggered SDMA
+// Plans" (Iris pull request).
+//
+// The pages' copy engine is a DMA engine fed, per peer, one in-order queue of
+// "poll the chunk's gate >= round, copy each region, add 1 to the peer's
+// arrival counter" chains ([TP] opening diagram; [PR] Design notes).  Here
+// the engine is a persistent kernel on the same GPU:
+//
+//  * Work units ("pieces") are whole rows of one region, about piece_bytes
+//    each, listed per source rank in schedule order.  CTAs claim pieces of a
+//    source with an atomic ticket, so the pieces of one chunk spread over many
+//    CUs while claims stay in schedule order.
+//  * A CTA reading a chunk for the first time polls its gate (low 32 bits of
+//    `ready` >= round) and then acquires at system scope, so the chunk's data
+//    is read after the producer's release.
+//  * A piece is read once and written to all P-1 other replicas (fan-out): the
+//    P per-peer queues of one source see the same gates, so they advance
+//    together and delivering to all of them at once changes no outcome.
+//  * The CTA finishing a chunk's last piece signals it: it waits until every
+//    earlier chunk of the same source has been signalled (head-of-line order,
+//    [TP] contract item 1), releases, adds 1 to `arrival` in every receiver's
+//    gate row, and advances the queue cursors.
+//
+// Every poll loop also watches an abort word in pinned host memory and a
+// wall-clock backstop, so every wave of the engine exits even when a gate
+// never opens.  A round interrupted that way is resumed by launching the
+// engine again: pieces are re-copied (same bytes), chunks already signalled
+// are not signalled twice.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "internal.h"
+#include "plan_internal.h"
+#include "tc.h"
+#include "tc_device.h"
+
+using tc::fail;
+
+namespace tc {
+
+// ------------------------------------------------------------ layout
+
+Layout compute_layout(uint32_t P, uint32_t G, uint64_t npieces) {
+  Layout L{};
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) {
+    const uint64_t at = off;
+    off = align_up(off + std::max<uint64_t>(bytes, 1), 256);
+    return at;
+  };
+  L.gate_stride = align_up((uint64_t)std::max<uint32_t>(G, 1) * TC_GATE_ROW_BYTES, 256);
+  L.gates = take(L.gate_stride * P);
+  L.pieces = take(npieces * sizeof(PieceD));
+  L.chunks = take((uint64_t)G * sizeof(ChunkD));
+  L.writers = take((uint64_t)G * 4);
+  L.wprefix = take((uint64_t)(G + 1) * 8);
+  L.launch_bytes = align_up((uint64_t)P * kTicketStride * 4 + kStatsWords * 8 + (uint64_t)G * 4, 256);
+  L.launch[0] = take(L.launch_bytes);
+  L.launch[1] = take(L.launch_bytes);
+  L.round_bytes = align_up((uint64_t)P * kTicketStride * 4 + (uint64_t)P * P * 4, 256);
+  L.round_blk[0] = take(L.round_bytes);
+  L.round_blk[1] = take(L.round_bytes);
+  L.status = take(256);
+  L.check = take((uint64_t)std::max<uint32_t>(G, 1) * 4);
+  L.total = off;
+  return L;
+}
+
+// ------------------------------------------------------------ kernels
+
+__global__ void zero_words_kernel(uint32_t* p, uint64_t n) {
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (uint64_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kEngineThreads = 256;
+constexpr int kUnroll = 8;
+constexpr uint32_t kStopCheckEvery = 64;
+
+struct EngineArgs {
+  uint64_t rep[TC_MAX_RANKS];
+  const PieceD* pieces;
+  const ChunkD* chunks;
+  uint8_t* gates;
+  uint64_t gate_stride;
+  uint32_t* tickets;      // this launch: one per source, kTicketStride apart
+  uint32_t* done;         // this launch: pieces finished, per chunk
+  uint64_t* stats;        // this launch: [0] ~first gate seen, [1] last signal
+  uint32_t* zero_launch;  // the other launch block, cleared for the next launch
+  uint32_t zero_launch_words;
+  uint32_t zero_round_words;
+  uint32_t* sig;          // this round: chunks signalled per source, kTicketStride apart
+  uint32_t* cur;          // this round: cursor[p*P + q]
+  uint32_t* zero_round;   // the other round block, cleared for the next round
+  const uint32_t* abort_word;  // pinned host word: launches <= it must stop
+  uint32_t* status;
+  uint32_t piece_base[TC_MAX_RANKS + 1];
+  uint32_t round;
+  uint32_t nranks;
+  uint32_t launch_id;
+  uint32_t pad;
+  uint64_t backstop_ticks;
+};
+
+__device__ inline uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
+
+// Leader only: true when this launch must give up (host abort or backstop).
+__device__ inline bool must_stop(const EngineArgs& a, uint64_t t0) {
+  const uint32_t ab = __hip_atomic_load(a.abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  if (ab >= a.launch_id) {
+    __hip_atomic_fetch_or(a.status, kStatusAborted, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    return true;
+  }
+  if (now_ticks() - t0 > a.backstop_ticks) {
+    __hip_atomic_fetch_or(a.status, kStatusExpired, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    return true;
+  }
+  return false;
+}
+
+// Leader only: spin until the u32 at `word` is >= target, then acquire.
+__device__ inline bool poll_ge(const EngineArgs& a, const uint32_t* word, uint32_t target,
+                               uint64_t t0, uint32_t* seen) {
+  uint32_t spins = 0;
+  for (;;) {
+    const uint32_t v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (v >= target) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+      if (seen) *seen = v;
+      return true;
+    }
+    if (++spins % kStopCheckEvery == 0 && must_stop(a, t0)) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+__device__ inline tc_gate_row* gate_row(const EngineArgs& a, uint32_t table, uint32_t g) {
+  return reinterpret_cast<tc_gate_row*>(a.gates + (uint64_t)table * a.gate_stride +
+                                        (uint64_t)g * TC_GATE_ROW_BYTES);
+}
+
+// Leader only: signal chunk `c` (global id g) of source p once every earlier
+// chunk of p has been signalled.
+__device__ bool signal_in_order(const EngineArgs& a, uint32_t p, uint32_t c, uint32_t g,
+                                uint64_t t0) {
+  uint32_t* sig = a.sig + p * kTicketStride;
+  uint32_t seen = 0;
+  if (!poll_ge(a, sig, c, t0, &seen)) return false;
+  if (seen > c) return true;  // signalled by an earlier launch of this round
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");  // every piece's bytes are in memory
+  for (uint32_t q = 0; q < a.nranks; ++q) {
+    if (q == p) continue;
+    __hip_atomic_fetch_add(&gate_row(a, q, g)->arrival, (uint64_t)1, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(a.cur + p * a.nranks + q, c + 1, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+  __hip_atomic_fetch_max(&a.stats[1], now_ticks(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(sig, c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  return true;
+}
+
+// Whole CTA: copy `len` bytes at `off` of replica p to every other replica.
+__device__ void copy_linear(const EngineArgs& a, uint32_t p, uint64_t off, uint64_t len) {
+  const uint32_t tid = threadIdx.x;
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(a.rep[p]);
+  uint64_t head = (16 - (off & 15)) & 15;
+  if (head > len) head = len;
+  const uint64_t body = (len - head) & ~(uint64_t)15;
+  const uint64_t tail = len - head - body;
+  if (tid < head + tail) {  // the unaligned bytes at both ends
+    const uint64_t b = tid < head ? off + tid : off + head + body + (tid - head);
+    const uint8_t v = src[b];
+    for (uint32_t q = 0; q < a.nranks; ++q)
+      if (q != p) reinterpret_cast<uint8_t*>(a.rep[q])[b] = v;
+  }
+  const uint64_t nv = body / 16;
+  const uint64_t start = off + head;
+  const u32x4* s4 = reinterpret_cast<const u32x4*>(src + start);
+  for (uint64_t base = 0; base < nv; base += (uint64_t)kEngineThreads * kUnroll) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint64_t i = base + (uint64_t)u * kEngineThreads + tid;
+      if (i < nv) v[u] = __builtin_nontemporal_load(s4 + i);
+    }
+    for (uint32_t q = 0; q < a.nranks; ++q) {
+      if (q == p) continue;
+      u32x4* d4 = reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(a.rep[q]) + start);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const uint64_t i = base + (uint64_t)u * kEngineThreads + tid;
+        if (i < nv) __builtin_nontemporal_store(v[u], d4 + i);
+      }
+    }
+  }
+}
+
+// Whole CTA: copy a 2-D piece (rows x row_bytes at pitch).
+__device__ void copy_2d(const EngineArgs& a, uint32_t p, const PieceD& pc) {
+  const uint32_t tid = threadIdx.x;
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(a.rep[p]);
+  const bool vec = ((pc.off | pc.pitch | pc.row_bytes) & 15) == 0;
+  if (vec) {
+    const uint32_t vpr = pc.row_bytes / 16;
+    const uint32_t nv = pc.rows * vpr;
+    for (uint32_t base = 0; base < nv; base += kEngineThreads * kUnroll) {
+      u32x4 v[kUnroll];
+      uint64_t at[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const uint32_t i = base + u * kEngineThreads + tid;
+        const uint32_t r = i / vpr, c = i - r * vpr;
+        at[u] = pc.off + (uint64_t)r * pc.pitch + (uint64_t)c * 16;
+        if (i < nv) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + at[u]));
+      }
+      for (uint32_t q = 0; q < a.nranks; ++q) {
+        if (q == p) continue;
+        uint8_t* dst = reinterpret_cast<uint8_t*>(a.rep[q]);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const uint32_t i = base + u * kEngineThreads + tid;
+          if (i < nv) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(dst + at[u]));
+        }
+      }
+    }
+  } else {
+    const uint32_t n = pc.rows * pc.row_bytes;
+    for (uint32_t i = tid; i < n; i += kEngineThreads) {
+      const uint32_t r = i / pc.row_bytes, c = i - r * pc.row_bytes;
+      const uint64_t b = pc.off + (uint64_t)r * pc.pitch + c;
+      const uint8_t v = src[b];
+      for (uint32_t q = 0; q < a.nranks; ++q)
+        if (q != p) reinterpret_cast<uint8_t*>(a.rep[q])[b] = v;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kEngineThreads) void engine_kernel(EngineArgs a) {
+  __shared__ uint32_t s_word;
+  __shared__ uint32_t s_ok;
+  const uint32_t tid = threadIdx.x;
+
+  // Clear the blocks the next launch and the next round will use; nothing
+  // touches them while this launch runs.
+  for (uint32_t i = blockIdx.x * kEngineThreads + tid; i < a.zero_launch_words;
+       i += gridDim.x * kEngineThreads)
+    a.zero_launch[i] = 0;
+  for (uint32_t i = blockIdx.x * kEngineThreads + tid; i < a.zero_round_words;
+       i += gridDim.x * kEngineThreads)
+    a.zero_round[i] = 0;
+
+  const uint64_t t0 = now_ticks();
+  uint32_t acquired = 0xFFFFFFFFu;  // last chunk whose gate this CTA has acquired
+
+  for (uint32_t s = 0; s < a.nranks; ++s) {
+    const uint32_t p = (blockIdx.x + s) % a.nranks;
+    const uint32_t np = a.piece_base[p + 1] - a.piece_base[p];
+    if (np == 0) continue;
+    for (;;) {
+      if (tid == 0) s_word = atomicAdd(a.tickets + p * kTicketStride, 1u);
+      __syncthreads();
+      const uint32_t t = s_word;
+      __syncthreads();
+      if (t >= np) break;
+      const PieceD pc = a.pieces[a.piece_base[p] + t];
+      const ChunkD cd = a.chunks[pc.chunk];
+      if (pc.chunk != acquired) {
+        if (tid == 0) {
+          const uint32_t* ready =
+              reinterpret_cast<const uint32_t*>(&gate_row(a, p, pc.chunk)->ready);
+          const bool ok = poll_ge(a, ready, a.round, t0, nullptr);
+          if (ok)
+            __hip_atomic_fetch_max(&a.stats[0], ~now_ticks(), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+          s_ok = ok;
+        }
+        __syncthreads();
+        if (!s_ok) return;
+        acquired = pc.chunk;
+      }
+      if (pc.rows == 1)
+        copy_linear(a, p, pc.off, pc.row_bytes);
+      else
+        copy_2d(a, p, pc);
+      __builtin_amdgcn_s_waitcnt(TC_WAITCNT_VMCNT0);  // this wave's stores are done
+      __syncthreads();                                // ... and every wave's
+      if (tid == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");  // write them back past this XCD's L2
+        const uint32_t old =
+            __hip_atomic_fetch_add(a.done + pc.chunk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        bool ok = true;
+        if (old + 1 == cd.npieces) {
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+          ok = signal_in_order(a, p, cd.local, pc.chunk, t0);
+        }
+        s_ok = ok;
+      }
+      __syncthreads();
+      if (!s_ok) return;
+    }
+  }
+}
+
+struct CheckArgs {
+  const ChunkD* chunks;
+  const uint8_t* gates;
+  uint64_t gate_stride;
+  uint32_t* flags;
+  uint32_t G, nranks, round, pad;
+};
+
+__device__ inline uint64_t ld(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// One thread per global chunk: compare its gate rows with what a complete
+// round r leaves ([TP] Gates and rounds: this rank's chunk marked ready and
+// arrived at every peer).
+__global__ void check_kernel(CheckArgs a) {
+  const uint32_t g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= a.G) return;
+  const ChunkD cd = a.chunks[g];
+  const uint64_t want = (uint64_t)a.round * cd.writers;
+  auto row = [&](uint32_t q) {
+    return reinterpret_cast<const tc_gate_row*>(a.gates + (uint64_t)q * a.gate_stride +
+                                                (uint64_t)g * TC_GATE_ROW_BYTES);
+  };
+  uint32_t f = 0;
+  const tc_gate_row* own = row(cd.rank);
+  const uint64_t w = ld(&own->writers);
+  if (w > want) f |= kFlagExtra;
+  if (w < want) f |= kFlagShortMarks;
+  if ((uint32_t)ld(&own->ready) < a.round) f |= kFlagNotOpen;
+  if (ld(&own->arrival) != 0) f |= kFlagCorrupt;
+  for (uint32_t q = 0; q < a.nranks; ++q) {
+    const tc_gate_row* r = row(q);
+    for (int k = 0; k < 5; ++k)
+      if (ld(&r->rsvd[k]) != 0) f |= kFlagCorrupt;
+    if (q == cd.rank) continue;
+    const uint64_t arr = ld(&r->arrival);
+    if (arr < a.round) f |= kFlagNotArrived;
+    if (arr > a.round) f |= kFlagCorrupt;
+    if (ld(&r->ready) != 0 || ld(&r->writers) != 0) f |= kFlagCorrupt;
+  }
+  a.flags[g] = f;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ host side
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(TC_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define TC_HIP(call)                                   \
+  do {                                                 \
+    hipError_t e_ = (call);                            \
+    if (e_ != hipSuccess) return hip_fail(e_, #call);  \
+  } while (0)
+
+static int zero_device(void* p, uint64_t bytes, hipStream_t s) {
+  const uint64_t words = bytes / 4;
+  if (words == 0) return TC_OK;
+  const uint32_t blocks = (uint32_t)std::min<uint64_t>((words + 255) / 256, 4096);
+  hipLaunchKernelGGL(zero_words_kernel, dim3(blocks), dim3(256), 0, s, (uint32_t*)p, words);
+  TC_HIP(hipGetLastError());
+  return TC_OK;
+}
+
+static int launch_engine(tc_plan* P) {
+  const Layout& L = P->L;
+  EngineArgs a{};
+  for (uint32_t p = 0; p < P->P; ++p) a.rep[p] = (uint64_t)P->rep[p];
+  a.pieces = reinterpret_cast<const PieceD*>(P->ws + L.pieces);
+  a.chunks = reinterpret_cast<const ChunkD*>(P->ws + L.chunks);
+  a.gates = P->ws + L.gates;
+  a.gate_stride = L.gate_stride;
+  const uint32_t lb = P->launch_seq & 1u;  // launch block of this launch
+  uint8_t* cur_launch = P->ws + L.launch[lb];
+  a.tickets = reinterpret_cast<uint32_t*>(cur_launch);
+  a.stats = reinterpret_cast<uint64_t*>(cur_launch + (uint64_t)P->P * kTicketStride * 4);
+  a.done = reinterpret_cast<uint32_t*>(cur_launch + (uint64_t)P->P * kTicketStride * 4 + kStatsWords * 8);
+  a.zero_launch = reinterpret_cast<uint32_t*>(P->ws + L.launch[lb ^ 1u]);
+  a.zero_launch_words = (uint32_t)(L.launch_bytes / 4);
+  const uint32_t rb = P->round & 1u;
+  uint8_t* cur_round = P->ws + L.round_blk[rb];
+  a.sig = reinterpret_cast<uint32_t*>(cur_round);
+  a.cur = reinterpret_cast<uint32_t*>(cur_round + (uint64_t)P->P * kTicketStride * 4);
+  a.zero_round = reinterpret_cast<uint32_t*>(P->ws + L.round_blk[rb ^ 1u]);
+  a.zero_round_words = (uint32_t)(L.round_bytes / 4);
+  a.abort_word = P->abort_dev;
+  a.status = reinterpret_cast<uint32_t*>(P->ws + L.status);
+  for (uint32_t p = 0; p <= P->P; ++p) a.piece_base[p] = P->piece_base[p];
+  a.round = P->round;
+  a.nranks = P->P;
+  a.launch_id = ++P->launch_id;
+  a.backstop_ticks = P->backstop_ticks;
+  P->cur_launch_block = lb;
+  P->launch_seq++;
+  TC_HIP(hipEventRecord(P->ev_engine_start, P->engine_stream));
+  hipLaunchKernelGGL(engine_kernel, dim3(P->engine_ctas), dim3(kEngineThreads), 0, P->engine_stream, a);
+  TC_HIP(hipGetLastError());
+  TC_HIP(hipEventRecord(P->ev_engine_done, P->engine_stream));
+  P->launches_this_round++;
+  return TC_OK;
+}
+
+// Runs the check kernel on the engine stream and reads the flags back.
+static int run_check(tc_plan* P) {
+  CheckArgs c{};
+  c.chunks = reinterpret_cast<const ChunkD*>(P->ws + P->L.chunks);
+  c.gates = P->ws + P->L.gates;
+  c.gate_stride = P->L.gate_stride;
+  c.flags = reinterpret_cast<uint32_t*>(P->ws + P->L.check);
+  c.G = P->G;
+  c.nranks = P->P;
+  c.round = P->round;
+  if (P->G > 0) {
+    hipLaunchKernelGGL(check_kernel, dim3((P->G + 255) / 256), dim3(256), 0, P->engine_stream, c);
+    TC_HIP(hipGetLastError());
+    TC_HIP(hipMemcpyAsync(P->flags_host, c.flags, (size_t)P->G * 4, hipMemcpyDeviceToHost,
+                          P->engine_stream));
+  }
+  TC_HIP(hipMemcpyAsync(P->status_host, P->ws + P->L.status, 4, hipMemcpyDeviceToHost,
+                        P->engine_stream));
+  TC_HIP(hipStreamSynchronize(P->engine_stream));
+  return TC_OK;
+}
+
+// Spins until `ev` completes or the deadline passes.  1 = done, 0 = deadline.
+static int event_done_by(hipEvent_t ev, std::chrono::steady_clock::time_point deadline,
+                         hipError_t* err) {
+  int spins = 0;
+  for (;;) {
+    const hipError_t e = hipEventQuery(ev);
+    if (e == hipSuccess) return 1;
+    if (e != hipErrorNotReady) {
+      *err = e;
+      return -1;
+    }
+    if (std::chrono::steady_clock::now() >= deadline) return 0;
+    if (++spins > 2000) std::this_thread::sleep_for(std::chrono::microseconds(20));
+  }
+}
+
+}  // namespace tc
+
+using namespace tc;
+
+extern "C" {
+
+int tc_plan_workspace_bytes(uint32_t nranks, const tc_schedule* const* schedules,
+                            uint64_t piece_bytes, uint64_t* out_bytes) {
+  if (!out_bytes || nranks == 0 || nranks > TC_MAX_RANKS)
+    return fail(TC_EINVAL, "workspace_bytes: bad rank count or NULL out");
+  if (piece_bytes == 0) piece_bytes = kDefaultPieceBytes;
+  std::vector<PieceD> pieces;
+  std::vector<ChunkD> chunks;
+  std::vector<uint32_t> pb, cb;
+  build_pieces(nranks, schedules, piece_bytes, pieces, chunks, pb, cb);
+  *out_bytes = compute_layout(nranks, (uint32_t)chunks.size(), pieces.size()).total;
+  return TC_OK;
+}
+
+int tc_plan_validate(const tc_plan_desc* d) {
+  if (!d) return fail(TC_EINVAL, "desc is NULL");
+  if (d->nranks == 0 || d->nranks > TC_MAX_RANKS)
+    return fail(TC_EINVAL, "nranks must be in 1.." + std::to_string(TC_MAX_RANKS));
+  if (d->buffer_bytes == 0) return fail(TC_EINVAL, "buffer_bytes is 0");
+  if ((d->flags & TC_CHECK_OWN_ROWS) && d->rows_per_rank_bytes == 0)
+    return fail(TC_EINVAL, "TC_CHECK_OWN_ROWS needs rows_per_rank_bytes");
+  if (d->piece_bytes && (d->piece_bytes % 256 || d->piece_bytes > (1ull << 31)))
+    return fail(TC_EINVAL, "piece_bytes must be a multiple of 256 and at most 2 GiB");
+  uint64_t G = 0;
+  for (uint32_t p = 0; p < d->nranks; ++p)
+    if (d->schedules && d->schedules[p]) G += d->schedules[p]->chunks.size();
+  if (G >= (1ull << 31)) return fail(TC_EINVAL, "too many chunks");
+  return validate_schedules(d->nranks, d->schedules, d->buffer_bytes,
+                            (d->flags & TC_CHECK_OWN_ROWS) != 0, d->rows_per_rank_bytes);
+}
+
+static void destroy(tc_plan* P) {
+  if (!P) return;
+  if (P->engine_stream) (void)hipStreamDestroy(P->engine_stream);
+  if (P->aux_stream) (void)hipStreamDestroy(P->aux_stream);
+  for (hipEvent_t e : {P->ev_prod_start, P->ev_prod_end, P->ev_engine_start, P->ev_engine_done})
+    if (e) (void)hipEventDestroy(e);
+  if (P->abort_host) (void)hipHostFree((void*)P->abort_host);
+  if (P->flags_host) (void)hipHostFree(P->flags_host);
+  if (P->status_host) (void)hipHostFree(P->status_host);
+  delete P;
+}
+
+int tc_plan_create(const tc_plan_desc* d, tc_plan** out) {
+  if (!out) return fail(TC_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (int rc = tc_plan_validate(d)) return rc;
+  if (!d->replicas || !d->workspace) return fail(TC_EINVAL, "replicas or workspace is NULL");
+  for (uint32_t p = 0; p < d->nranks; ++p)
+    if (!d->replicas[p] || ((uintptr_t)d->replicas[p] & 255))
+      return fail(TC_EINVAL, "replica pointers must be non-NULL and 256-byte aligned");
+  if ((uintptr_t)d->workspace & 255) return fail(TC_EINVAL, "workspace must be 256-byte aligned");
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev == 0) return fail(TC_ENODEV, "no GPU visible");
+
+  auto* P = new tc_plan();
+  P->P = d->nranks;
+  P->buffer_bytes = d->buffer_bytes;
+  for (uint32_t p = 0; p < d->nranks; ++p) P->rep[p] = (uint8_t*)d->replicas[p];
+  P->ws = (uint8_t*)d->workspace;
+  P->ws_bytes = d->workspace_bytes;
+  const uint64_t piece_bytes = d->piece_bytes ? d->piece_bytes : kDefaultPieceBytes;
+  build_pieces(P->P, d->schedules, piece_bytes, P->pieces, P->chunks, P->piece_base, P->chunk_base);
+  P->G = (uint32_t)P->chunks.size();
+  P->L = compute_layout(P->P, P->G, P->pieces.size());
+  if (P->L.total > d->workspace_bytes) {
+    const uint64_t need = P->L.total;
+    delete P;
+    return fail(TC_ENOMEM, "workspace too small: need " + std::to_string(need) + " bytes");
+  }
+  auto bail = [&](int rc) {
+    destroy(P);
+    return rc;
+  };
+  int rc = TC_OK;
+#define TC_HIP_C(call)                                       \
+  do {                                                       \
+    hipError_t e_ = (call);                                  \
+    if (e_ != hipSuccess) return bail(hip_fail(e_, #call));  \
+  } while (0)
+  TC_HIP_C(hipGetDevice(&P->device));
+  int cus = 0;
+  TC_HIP_C(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, P->device));
+  // The engine is launched before the producer it waits for, so it must not
+  // share a hardware queue with the producer's stream (kernels of streams
+  // that share one run in submission order).  A CU-masked stream always gets
+  // a queue of its own, so the engine stream is always created with a mask:
+  // the caller's, or every CU.
+  std::vector<uint32_t> mask;
+  if (d->cu_mask && d->cu_mask_words) {
+    mask.assign(d->cu_mask, d->cu_mask + d->cu_mask_words);
+  } else {
+    mask.assign((cus + 31) / 32, 0u);
+    for (int i = 0; i < cus; ++i) mask[i / 32] |= 1u << (i % 32);
+  }
+  uint32_t usable = 0;
+  for (uint32_t m : mask) usable += __builtin_popcount(m);
+  if (usable == 0) return bail(fail(TC_EINVAL, "cu_mask selects no CU"));
+  TC_HIP_C(hipExtStreamCreateWithCUMask(&P->engine_stream, (uint32_t)mask.size(), mask.data()));
+  TC_HIP_C(hipStreamCreateWithFlags(&P->aux_stream, hipStreamNonBlocking));
+  TC_HIP_C(hipEventCreateWithFlags(&P->ev_prod_start, hipEventDisableTiming));
+  TC_HIP_C(hipEventCreateWithFlags(&P->ev_prod_end, hipEventDisableTiming));
+  TC_HIP_C(hipEventCreate(&P->ev_engine_start));
+  TC_HIP_C(hipEventCreate(&P->ev_engine_done));
+  void* hp = nullptr;
+  TC_HIP_C(hipHostMalloc(&hp, 64, hipHostMallocMapped | hipHostMallocCoherent));
+  P->abort_host = (volatile uint32_t*)hp;
+  P->abort_host[0] = 0;
+  TC_HIP_C(hipHostGetDevicePointer((void**)&P->abort_dev, hp, 0));
+  TC_HIP_C(hipHostMalloc((void**)&P->flags_host, (size_t)std::max<uint32_t>(P->G, 1) * 4, 0));
+  TC_HIP_C(hipHostMalloc((void**)&P->status_host, 64, 0));
+
+  // Zero the workspace (gates start at zero, [TP] Gates and rounds), then
+  // upload the descriptors once.
+  if ((rc = zero_device(P->ws, P->L.total, P->engine_stream))) return bail(rc);
+  TC_HIP_C(hipStreamSynchronize(P->engine_stream));
+  std::vector<uint32_t> writers(P->G);
+  std::vector<uint64_t> wprefix(P->G + 1, 0);
+  for (uint32_t g = 0; g < P->G; ++g) {
+    writers[g] = P->chunks[g].writers;
+    wprefix[g + 1] = wprefix[g] + writers[g];
+  }
+  P->total_writers = wprefix[P->G];
+  if (!P->pieces.empty())
+    TC_HIP_C(hipMemcpy(P->ws + P->L.pieces, P->pieces.data(), P->pieces.size() * sizeof(PieceD),
+                       hipMemcpyHostToDevice));
+  if (P->G) {
+    TC_HIP_C(hipMemcpy(P->ws + P->L.chunks, P->chunks.data(), P->G * sizeof(ChunkD),
+                       hipMemcpyHostToDevice));
+    TC_HIP_C(hipMemcpy(P->ws + P->L.writers, writers.data(), P->G * 4, hipMemcpyHostToDevice));
+  }
+  TC_HIP_C(hipMemcpy(P->ws + P->L.wprefix, wprefix.data(), wprefix.size() * 8, hipMemcpyHostToDevice));
+
+  const uint32_t npieces = (uint32_t)P->pieces.size();
+  P->engine_ctas = d->engine_ctas ? d->engine_ctas : 2 * usable;
+  P->engine_ctas = std::max<uint32_t>(1, std::min<uint32_t>(P->engine_ctas, std::max<uint32_t>(npieces, 1)));
+  const uint64_t backstop_us = d->engine_backstop_us ? d->engine_backstop_us : 30ull * 1000 * 1000;
+  P->backstop_ticks = backstop_us * 100;  // s_memrealtime runs at 100 MHz
+  for (const ChunkD& c : P->chunks) {
+    P->bytes_read += c.bytes;
+    P->bytes_moved += c.bytes * (P->P - 1);
+  }
+  P->round = 1;
+  P->state = TC_STATE_READY;
+#undef TC_HIP_C
+  *out = P;
+  return TC_OK;
+}
+
+int tc_plan_start(tc_plan* P, void* stream, tc_handle* out) {
+  if (!P || !out) return fail(TC_EINVAL, "start: NULL argument");
+  if (P->state != TC_STATE_READY) return fail(TC_ESTATE, "start() needs a READY plan");
+  hipStream_t ps = (hipStream_t)stream;
+  if (ps == nullptr || ps == hipStreamLegacy)
+    return fail(TC_EINVAL, "start: the legacy default stream waits for every blocking stream, "
+                           "the copy engine's included; run the producer on another stream");
+  // The copies of this round may overwrite the replicas: order the engine
+  // after everything already queued on the producer's stream.
+  TC_HIP(hipEventRecord(P->ev_prod_start, ps));
+  TC_HIP(hipStreamWaitEvent(P->engine_stream, P->ev_prod_start, 0));
+  P->producer_stream = ps;
+  P->launches_this_round = 0;
+  P->need_relaunch = false;
+  P->problems.clear();
+  if (int rc = launch_engine(P)) return rc;
+  P->state = TC_STATE_STARTED;
+  fill_handle(P, out);
+  return TC_OK;
+}
+
+int tc_plan_wait(tc_plan* P, uint64_t timeout_us) {
+  if (!P) return fail(TC_EINVAL, "wait: NULL plan");
+  if (P->state != TC_STATE_STARTED) return fail(TC_ESTATE, "wait() needs a STARTED plan");
+  P->problems.clear();
+  if (P->need_relaunch) {  // resume a round a timeout interrupted
+    if (int rc = launch_engine(P)) return rc;
+    P->need_relaunch = false;
+  }
+  TC_HIP(hipEventRecord(P->ev_prod_end, P->producer_stream));
+  const auto deadline = std::chrono::steady_clock::now() + std::chrono::microseconds(timeout_us);
+  hipError_t err = hipSuccess;
+  int e1 = event_done_by(P->ev_engine_done, deadline, &err);
+  int e2 = e1 == 1 ? event_done_by(P->ev_prod_end, deadline, &err) : 0;
+  if (e1 < 0 || e2 < 0) return hip_fail(err, "hipEventQuery");
+  bool timed_out = !(e1 == 1 && e2 == 1);
+  if (timed_out && e1 != 1) {
+    // Stop this launch of the engine; every poll loop watches the word.
+    __atomic_store_n(P->abort_host, P->launch_id, __ATOMIC_SEQ_CST);
+    const auto drain = std::chrono::steady_clock::now() + std::chrono::seconds(10);
+    int e3 = event_done_by(P->ev_engine_done, drain, &err);
+    if (e3 < 0) return hip_fail(err, "hipEventQuery");
+    if (e3 == 0)
+      return fail(TC_ETIMEOUT, "wait: copy engine did not stop within 10 s of the abort");
+  }
+  TC_HIP(hipEventElapsedTime(&P->last_engine_ms, P->ev_engine_start, P->ev_engine_done));
+  if (int rc = run_check(P)) return rc;
+  const uint32_t st = P->status_host[0];
+  if (st & (kStatusAborted | kStatusExpired)) P->need_relaunch = true;
+  // Clear the status word for the next launch (a fill kernel, not a memset).
+  if (int rc = zero_device(P->ws + P->L.status, 4, P->engine_stream)) return rc;
+  bool extra = false, corrupt = false, shortc = false;
+  for (uint32_t g = 0; g < P->G; ++g) {
+    const uint32_t f = P->flags_host[g];
+    if (f & kFlagExtra) extra = true;
+    if (f & kFlagCorrupt) corrupt = true;
+    if (f & (kFlagShortMarks | kFlagNotOpen | kFlagNotArrived)) shortc = true;
+  }
+  auto collect = [&](uint32_t mask) {
+    for (uint32_t g = 0; g < P->G; ++g)
+      if (P->flags_host[g] & mask) {
+        P->problems.push_back(P->chunks[g].rank);
+        P->problems.push_back(P->chunks[g].local);
+      }
+  };
+  if (extra) {
+    collect(kFlagExtra);
+    P->state = TC_STATE_FAILED;
+    return fail(TC_EEXTRA, "wait: chunks got more marks than their writers this round");
+  }
+  if (corrupt) {
+    collect(kFlagCorrupt);
+    P->state = TC_STATE_FAILED;
+    return fail(TC_ECORRUPT, "wait: gate rows hold values no correct round produces");
+  }
+  if (shortc || timed_out || P->need_relaunch) {
+    collect(kFlagShortMarks | kFlagNotOpen | kFlagNotArrived);
+    if (!P->need_relaunch && shortc) P->need_relaunch = true;
+    return fail(TC_ETIMEOUT, "wait: timed out with " + std::to_string(P->problems.size() / 2) +
+                                 " chunk(s) still short");
+  }
+  P->state = TC_STATE_DONE;
+  return TC_OK;
+}
+
+int tc_plan_next_round(tc_plan* P) {
+  if (!P) return fail(TC_EINVAL, "next_round: NULL plan");
+  if (P->state != TC_STATE_DONE) return fail(TC_ESTATE, "next_round() needs a DONE plan");
+  if (P->round >= TC_ROUND_LIMIT) return fail(TC_EROUNDS, "round limit 2^32-1 reached");
+  P->round++;
+  P->state = TC_STATE_READY;
+  return TC_OK;
+}
+
+int tc_plan_close(tc_plan* P) {
+  if (!P) return TC_OK;
+  int rc = TC_OK;
+  if (P->launch_id) {
+    __atomic_store_n(P->abort_host, P->launch_id, __ATOMIC_SEQ_CST);
+    hipError_t err = hipSuccess;
+    const auto drain = std::chrono::steady_clock::now() + std::chrono::seconds(10);
+    if (event_done_by(P->ev_engine_done, drain, &err) != 1)
+      rc = fail(TC_ETIMEOUT, "close: copy engine did not stop within 10 s");
+    else
+      (void)hipStreamSynchronize(P->engine_stream);
+  }
+  if (rc == TC_OK) destroy(P);  // on failure leak rather than free memory a kernel may touch
+  return rc;
+}
+
+int tc_plan_state(const tc_plan* P, int* state, uint32_t* round) {
+  if (!P) return fail(TC_EINVAL, "state: NULL plan");
+  if (state) *state = P->state;
+  if (round) *round = P->round;
+  return TC_OK;
+}
+
+int tc_plan_problems(const tc_plan* P, uint32_t* rank_chunk, uint32_t cap, uint32_t* n) {
+  if (!P) return fail(TC_EINVAL, "problems: NULL plan");
+  const uint32_t total = (uint32_t)(P->problems.size() / 2);
+  if (n) *n = total;
+  if (rank_chunk)
+    for (uint32_t i = 0; i < std::min(cap, total); ++i) {
+      rank_chunk[2 * i] = P->problems[2 * i];
+      rank_chunk[2 * i + 1] = P->problems[2 * i + 1];
+    }
+  return TC_OK;
+}
+
+int tc_plan_read_gates(tc_plan* P, void* host, uint64_t bytes) {
+  if (!P || !host) return fail(TC_EINVAL, "read_gates: NULL argument");
+  const uint64_t need = (uint64_t)P->P * P->G * TC_GATE_ROW_BYTES;
+  if (bytes < need) return fail(TC_EINVAL, "read_gates: need " + std::to_string(need) + " bytes");
+  for (uint32_t q = 0; q < P->P && P->G; ++q)
+    TC_HIP(hipMemcpyAsync((uint8_t*)host + (uint64_t)q * P->G * TC_GATE_ROW_BYTES,
+                          P->ws + P->L.gates + q * P->L.gate_stride,
+                          (size_t)P->G * TC_GATE_ROW_BYTES, hipMemcpyDeviceToHost, P->aux_stream));
+  TC_HIP(hipStreamSynchronize(P->aux_stream));
+  return TC_OK;
+}
+
+int tc_plan_read_cursors(tc_plan* P, uint32_t* host) {
+  if (!P || !host) return fail(TC_EINVAL, "read_cursors: NULL argument");
+  const uint8_t* blk = P->ws + P->L.round_blk[P->round & 1u];
+  TC_HIP(hipMemcpyAsync(host, blk + (uint64_t)P->P * kTicketStride * 4, (size_t)P->P * P->P * 4,
+                        hipMemcpyDeviceToHost, P->aux_stream));
+  TC_HIP(hipStreamSynchronize(P->aux_stream));
+  return TC_OK;
+}
+
+int tc_plan_stats(tc_plan* P, tc_stats* out) {
+  if (!P || !out) return fail(TC_EINVAL, "stats: NULL argument");
+  std::memset(out, 0, sizeof(*out));
+  out->engine_ms = P->last_engine_ms;
+  out->launches = P->launches_this_round;
+  out->engine_ctas = P->engine_ctas;
+  out->bytes_moved = P->bytes_moved;
+  out->bytes_read = P->bytes_read;
+  out->pieces = P->pieces.size();
+  out->G = P->G;
+  if (P->launch_seq) {
+    uint64_t st[kStatsWords] = {0};
+    const uint8_t* blk = P->ws + P->L.launch[P->cur_launch_block];
+    TC_HIP(hipMemcpyAsync(st, blk + (uint64_t)P->P * kTicketStride * 4, sizeof(st),
+                          hipMemcpyDeviceToHost, P->aux_stream));
+    TC_HIP(hipStreamSynchronize(P->aux_stream));
+    const uint64_t first = ~st[0];
+    if (st[0] && st[1] >= first) out->window_ticks = st[1] - first;
+  }
+  return TC_OK;
+}
+
+int tc_plan_engine_stream(tc_plan* P, void** stream) {
+  if (!P || !stream) return fail(TC_EINVAL, "engine_stream: NULL argument");
+  *stream = (void*)P->engine_stream;
+  return TC_OK;
+}
+
+int tc_plan_debug_set_round(tc_plan* P, uint32_t round) {
+  if (!P) return fail(TC_EINVAL, "debug_set_round: NULL plan");
+  if (P->state != TC_STATE_DONE || round == 0)
+    return fail(TC_ESTATE, "debug_set_round: plan must be DONE and round >= 1");
+  P->round = round;
+  return TC_OK;
+}
+
+}  // extern "C"
+
+void tc::fill_handle(const tc_plan* P, tc_handle* h) {
+  std::memset(h, 0, sizeof(*h));
+  h->gates = (uint64_t)(P->ws + P->L.gates);
+  h->gate_stride = P->L.gate_stride;
+  h->writers = (uint64_t)(P->ws + P->L.writers);
+  h->round = P->round;
+  h->nranks = P->P;
+  for (uint32_t p = 0; p <= P->P; ++p) h->chunk_base[p] = P->chunk_base[p];
+  for (uint32_t p = P->P + 1; p <= TC_MAX_RANKS; ++p) h->chunk_base[p] = P->G;
+}

@@ -1,0 +1,82 @@
+// The plan object and its workspace layout (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <vector>
+
+#include "internal.h"
+#include "tc.h"
+
+namespace tc {
+
+constexpr uint32_t kTicketStride = 16;  // u32 words between per-source counters (64 B)
+constexpr uint32_t kStatsWords = 2;     // u64 words of per-launch timestamps
+
+constexpr uint32_t kStatusAborted = 1;  // engine stopped by the host's abort word
+constexpr uint32_t kStatusExpired = 2;  // engine stopped by its wall-clock backstop
+
+// Per-chunk flags written by the completion check.
+constexpr uint32_t kFlagExtra = 1;       // writer counter > round * writers
+constexpr uint32_t kFlagShortMarks = 2;  // writer counter < round * writers
+constexpr uint32_t kFlagNotOpen = 4;     // ready < round
+constexpr uint32_t kFlagNotArrived = 8;  // some receiver's arrival < round
+constexpr uint32_t kFlagCorrupt = 16;    // values no correct run produces
+
+// Byte offsets into the caller's workspace.
+struct Layout {
+  uint64_t gates, gate_stride;
+  uint64_t pieces, chunks, writers, wprefix;
+  uint64_t launch[2], launch_bytes;     // tickets | stats | done, per launch parity
+  uint64_t round_blk[2], round_bytes;   // sig | cursors, per round parity
+  uint64_t status;
+  uint64_t check;
+  uint64_t total;
+};
+
+Layout compute_layout(uint32_t P, uint32_t G, uint64_t npieces);
+
+}  // namespace tc
+
+struct tc_plan {
+  uint32_t P = 0, G = 0;
+  uint64_t buffer_bytes = 0;
+  uint8_t* rep[TC_MAX_RANKS] = {};
+  uint8_t* ws = nullptr;
+  uint64_t ws_bytes = 0;
+  tc::Layout L{};
+  std::vector<tc::PieceD> pieces;
+  std::vector<tc::ChunkD> chunks;
+  std::vector<uint32_t> piece_base, chunk_base;
+  uint64_t total_writers = 0;
+  uint64_t bytes_read = 0, bytes_moved = 0;
+
+  int device = 0;
+  hipStream_t engine_stream = nullptr;
+  hipStream_t aux_stream = nullptr;
+  hipStream_t producer_stream = nullptr;
+  hipEvent_t ev_prod_start = nullptr, ev_prod_end = nullptr;
+  hipEvent_t ev_engine_start = nullptr, ev_engine_done = nullptr;
+  volatile uint32_t* abort_host = nullptr;  // pinned, mapped
+  uint32_t* abort_dev = nullptr;
+  uint32_t* flags_host = nullptr;           // pinned
+  uint32_t* status_host = nullptr;          // pinned
+
+  uint32_t engine_ctas = 0;
+  uint64_t backstop_ticks = 0;
+  uint32_t round = 1;
+  int state = TC_STATE_READY;
+  uint32_t launch_id = 0;    // id of the newest engine launch (abort compares to it)
+  uint32_t launch_seq = 0;   // launches so far; parity picks the launch block
+  uint32_t cur_launch_block = 0;
+  uint32_t launches_this_round = 0;
+  bool need_relaunch = false;
+  float last_engine_ms = 0.f;
+  std::vector<uint32_t> problems;  // (rank, chunk) pairs
+};
+
+namespace tc {
+void fill_handle(const tc_plan* P, tc_handle* h);
+int hip_fail(hipError_t e, const char* what);
+}  // namespace tc

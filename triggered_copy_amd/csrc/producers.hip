@@ -1,0 +1,323 @@
+// Synthetic producers and the device-view consumer of a plan.
+//
+// [TP] = "Triggered Plans" (Iris documentation).  Producers write their part
+// of the output and mark each chunk ready once per writer (section Model;
+// The kernel author's contract, item 2); mark_ready is the device function of
+// section Memory ordering.  The consumer reads a chunk only after
+// arrived/wait (section Memory ordering, consumer side).
+//
+// Values: element i of rank p's view in round r holds
+//   h = mix64((p << 48) | (r << 32) | i) ^ mix64(seed)),
+// mix64 being SplitMix64's output function (Steele, Lea & Flood, OOPSLA 2014);
+// u32 = low 32 bits, u8 = low 8 bits, bf16 = high half of the fp32 value
+// ((h >> 41) - 2^22) * 2^-22, which lies in [-1, 1).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <string>
+
+#include "internal.h"
+#include "plan_internal.h"
+#include "tc.h"
+#include "tc_device.h"
+
+using tc::fail;
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kFillThreads = 256;
+
+__host__ __device__ inline uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+struct FillArgs {
+  uint64_t rep[TC_MAX_RANKS];
+  uint64_t view_off[TC_MAX_RANKS];     // byte offset of rank p's view
+  uint64_t view_pitch[TC_MAX_RANKS];   // bytes per view row (row_stride * elem)
+  uint64_t view_cols[TC_MAX_RANKS];
+  const tc::PieceD* pieces;
+  const tc::ChunkD* chunks;
+  const uint64_t* wprefix;             // G + 1 prefix sums of writers
+  const uint32_t* order;               // serial mode: [P][order_stride], or NULL
+  tc_handle h;
+  uint64_t seed_mix;
+  uint32_t contiguous;                 // bit p: view p has row_stride == cols
+  uint32_t kind, mark, elem;
+  uint32_t order_stride, G, pad0, pad1;
+};
+
+__device__ inline uint64_t key_hash(const FillArgs& a, uint32_t p, uint64_t idx) {
+  const uint64_t k = ((uint64_t)p << 48) | ((uint64_t)a.h.round << 32) | idx;
+  return mix64(k ^ a.seed_mix);
+}
+
+__device__ inline uint32_t bf16_of(uint64_t h) {
+  const int32_t u = (int32_t)(h >> 41) - (1 << 22);
+  const float f = (float)u * (1.0f / 4194304.0f);  // exact: |u| <= 2^22
+  return __float_as_uint(f) >> 16;
+}
+
+// Element index (within rank p's view) of the element at byte `off`.
+__device__ inline uint64_t index_at(const FillArgs& a, uint32_t p, uint64_t off) {
+  const uint64_t rel = off - a.view_off[p];
+  if (a.contiguous & (1u << p)) return rel / a.elem;
+  const uint64_t r = rel / a.view_pitch[p];
+  return r * a.view_cols[p] + (rel - r * a.view_pitch[p]) / a.elem;
+}
+
+// Whole CTA: write the values of `len` bytes at `off` (within one view row,
+// or anywhere in a contiguous view) of replica p.
+__device__ void fill_range(const FillArgs& a, uint32_t p, uint64_t off, uint64_t len) {
+  uint8_t* base = reinterpret_cast<uint8_t*>(a.rep[p]);
+  const uint64_t idx0 = index_at(a, p, off);
+  const uint32_t e = a.elem;
+  if (((off | len) & 15) == 0) {
+    const uint32_t per = 16 / e;  // elements per 16-byte vector
+    const uint64_t nv = len / 16;
+    u32x4* dst = reinterpret_cast<u32x4*>(base + off);
+    for (uint64_t v = threadIdx.x; v < nv; v += kFillThreads) {
+      const uint64_t i0 = idx0 + v * per;
+      u32x4 out;
+      if (a.kind == TC_FILL_U32) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) out[k] = (uint32_t)key_hash(a, p, i0 + k);
+      } else if (a.kind == TC_FILL_BF16) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          out[k] = bf16_of(key_hash(a, p, i0 + 2 * k)) | (bf16_of(key_hash(a, p, i0 + 2 * k + 1)) << 16);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          uint32_t w = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) w |= ((uint32_t)key_hash(a, p, i0 + 4 * k + b) & 0xFF) << (8 * b);
+          out[k] = w;
+        }
+      }
+      dst[v] = out;
+    }
+  } else {
+    const uint64_t n = len / e;
+    for (uint64_t i = threadIdx.x; i < n; i += kFillThreads) {
+      const uint64_t h = key_hash(a, p, idx0 + i);
+      uint8_t* d = base + off + i * e;
+      if (a.kind == TC_FILL_U32) {
+        const uint32_t v = (uint32_t)h;
+        for (uint32_t b = 0; b < 4; ++b) d[b] = (uint8_t)(v >> (8 * b));
+      } else if (a.kind == TC_FILL_BF16) {
+        const uint32_t v = bf16_of(h);
+        d[0] = (uint8_t)v;
+        d[1] = (uint8_t)(v >> 8);
+      } else {
+        d[0] = (uint8_t)h;
+      }
+    }
+  }
+}
+
+__device__ void fill_piece(const FillArgs& a, uint32_t p, const tc::PieceD& pc) {
+  for (uint32_t r = 0; r < pc.rows; ++r) fill_range(a, p, pc.off + (uint64_t)r * pc.pitch, pc.row_bytes);
+}
+
+// Writer j of chunk g writes pieces [j*np/w, (j+1)*np/w) of the chunk.
+__device__ void fill_share(const FillArgs& a, uint32_t g, uint32_t j) {
+  const tc::ChunkD cd = a.chunks[g];
+  const uint64_t lo = (uint64_t)j * cd.npieces / cd.writers;
+  const uint64_t hi = (uint64_t)(j + 1) * cd.npieces / cd.writers;
+  for (uint64_t k = lo; k < hi; ++k) fill_piece(a, cd.rank, a.pieces[cd.first_piece + k]);
+}
+
+// Largest g with wprefix[g] <= slot (binary search over G + 1 entries).
+__device__ inline uint32_t slot_chunk(const uint64_t* wprefix, uint32_t G, uint64_t slot) {
+  uint32_t lo = 0, hi = G;  // answer in [lo, hi)
+  while (hi - lo > 1) {
+    const uint32_t mid = (lo + hi) / 2;
+    if (wprefix[mid] <= slot) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(kFillThreads) void fill_parallel_kernel(FillArgs a) {
+  const uint64_t slot = blockIdx.x;
+  const uint32_t g = slot_chunk(a.wprefix, a.G, slot);
+  const uint32_t j = (uint32_t)(slot - a.wprefix[g]);
+  fill_share(a, g, j);
+  if (a.mark == TC_MARK_INKERNEL) {
+    const tc::ChunkD cd = a.chunks[g];
+    tc_mark_ready(a.h, cd.rank, cd.local);
+  }
+}
+
+// One CTA per rank: its chunks in order[], each writer's share in turn, a
+// mark after each share.
+__global__ __launch_bounds__(kFillThreads) void fill_serial_kernel(FillArgs a) {
+  const uint32_t p = blockIdx.x;
+  const uint32_t n = a.h.chunk_base[p + 1] - a.h.chunk_base[p];
+  for (uint32_t k = 0; k < n; ++k) {
+    const uint32_t c = a.order ? a.order[(uint64_t)p * a.order_stride + k] : k;
+    if (c >= n) continue;  // not a chunk of this rank: it gets no marks, wait() names it
+    const uint32_t g = a.h.chunk_base[p] + c;
+    const uint32_t w = a.chunks[g].writers;
+    for (uint32_t j = 0; j < w; ++j) {
+      fill_share(a, g, j);
+      if (a.mark == TC_MARK_INKERNEL) tc_mark_ready(a.h, p, c);
+    }
+  }
+}
+
+struct MarkArgs {
+  tc_handle h;
+  const uint64_t* wprefix;
+  const tc::ChunkD* chunks;
+  uint32_t G, rank, chunk, all;
+};
+
+__global__ __launch_bounds__(64) void mark_kernel(MarkArgs a) {
+  if (a.all) {
+    const uint32_t g = slot_chunk(a.wprefix, a.G, blockIdx.x);
+    const tc::ChunkD cd = a.chunks[g];
+    tc_mark_ready(a.h, cd.rank, cd.local);
+  } else {
+    tc_mark_ready(a.h, a.rank, a.chunk);
+  }
+}
+
+struct ConsumeArgs {
+  tc_handle h;
+  uint64_t rep_dst;
+  uint8_t* out;
+  const tc::PieceD* pieces;
+  const tc::ChunkD* chunks;
+  uint32_t* status;
+  uint32_t dst, max_polls;
+};
+
+// One CTA per global chunk: wait for its arrival at rank dst, then copy its
+// bytes from replica dst to out at the same offsets.
+__global__ __launch_bounds__(256) void consume_kernel(ConsumeArgs a) {
+  const uint32_t g = blockIdx.x;
+  const tc::ChunkD cd = a.chunks[g];
+  const bool ok = tc_wait(a.h, a.dst, cd.rank, cd.local, a.max_polls);
+  if (ok) {
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(a.rep_dst);
+    for (uint32_t k = 0; k < cd.npieces; ++k) {
+      const tc::PieceD pc = a.pieces[cd.first_piece + k];
+      const uint64_t n = (uint64_t)pc.rows * pc.row_bytes;
+      for (uint64_t i = threadIdx.x; i < n; i += blockDim.x) {
+        const uint64_t r = i / pc.row_bytes, c = i - r * pc.row_bytes;
+        const uint64_t b = pc.off + r * pc.pitch + c;
+        a.out[b] = src[b];
+      }
+    }
+  }
+  if (tc_is_cta_leader()) a.status[g] = ok ? 1u : 2u;
+}
+
+}  // namespace
+
+#define TC_HIP(call)                                       \
+  do {                                                     \
+    hipError_t e_ = (call);                                \
+    if (e_ != hipSuccess) return tc::hip_fail(e_, #call);  \
+  } while (0)
+
+extern "C" {
+
+int tc_produce_fill(tc_plan* P, const tc_handle* h, const tc_fill_desc* d, void* stream) {
+  if (!P || !h || !d || !d->views) return fail(TC_EINVAL, "fill: NULL argument");
+  const uint32_t elem = d->kind == TC_FILL_U32 ? 4 : d->kind == TC_FILL_BF16 ? 2 : d->kind == TC_FILL_U8 ? 1 : 0;
+  if (!elem) return fail(TC_EINVAL, "fill: unknown kind");
+  if (d->mark_mode > TC_MARK_NONE) return fail(TC_EINVAL, "fill: unknown mark mode");
+  if (h->round >= (1u << 16)) return fail(TC_EINVAL, "fill: value keys hold rounds below 65536");
+  if (P->state != TC_STATE_STARTED || h->round != P->round)
+    return fail(TC_ESTATE, "fill: the handle is not this plan's started round");
+  FillArgs a{};
+  for (uint32_t p = 0; p < P->P; ++p) {
+    const tc_view& v = d->views[p];
+    if (v.elem_bytes != elem) return fail(TC_EINVAL, "fill: view elem_bytes does not match kind");
+    if (v.rows * v.cols >= (1ull << 32)) return fail(TC_EINVAL, "fill: value keys hold < 2^32 elements");
+    a.rep[p] = (uint64_t)P->rep[p];
+    a.view_off[p] = v.byte_offset;
+    a.view_pitch[p] = v.row_stride * elem;
+    a.view_cols[p] = v.cols;
+    if (v.row_stride == v.cols) a.contiguous |= 1u << p;
+  }
+  a.pieces = reinterpret_cast<const tc::PieceD*>(P->ws + P->L.pieces);
+  a.chunks = reinterpret_cast<const tc::ChunkD*>(P->ws + P->L.chunks);
+  a.wprefix = reinterpret_cast<const uint64_t*>(P->ws + P->L.wprefix);
+  a.order = d->order;
+  a.order_stride = d->order_stride;
+  a.h = *h;
+  a.seed_mix = mix64(d->seed);
+  a.kind = d->kind;
+  a.mark = d->mark_mode;
+  a.elem = elem;
+  a.G = P->G;
+  hipStream_t s = (hipStream_t)stream;
+  if (d->serial) {
+    if (d->ctas_per_rank > 1) return fail(TC_EINVAL, "fill: serial mode runs one CTA per rank");
+    hipLaunchKernelGGL(fill_serial_kernel, dim3(P->P), dim3(kFillThreads), 0, s, a);
+  } else {
+    if (d->order) return fail(TC_EINVAL, "fill: an order needs serial mode");
+    if (P->total_writers == 0) return TC_OK;
+    if (P->total_writers > 0x7FFFFFFFull) return fail(TC_EINVAL, "fill: too many writers");
+    hipLaunchKernelGGL(fill_parallel_kernel, dim3((uint32_t)P->total_writers), dim3(kFillThreads), 0, s, a);
+  }
+  TC_HIP(hipGetLastError());
+  return TC_OK;
+}
+
+int tc_mark_all(tc_plan* P, const tc_handle* h, void* stream) {
+  if (!P || !h) return fail(TC_EINVAL, "mark_all: NULL argument");
+  if (P->total_writers == 0) return TC_OK;
+  if (P->total_writers > 0x7FFFFFFFull) return fail(TC_EINVAL, "mark_all: too many writers");
+  MarkArgs a{};
+  a.h = *h;
+  a.wprefix = reinterpret_cast<const uint64_t*>(P->ws + P->L.wprefix);
+  a.chunks = reinterpret_cast<const tc::ChunkD*>(P->ws + P->L.chunks);
+  a.G = P->G;
+  a.all = 1;
+  hipLaunchKernelGGL(mark_kernel, dim3((uint32_t)P->total_writers), dim3(64), 0, (hipStream_t)stream, a);
+  TC_HIP(hipGetLastError());
+  return TC_OK;
+}
+
+int tc_mark(tc_plan* P, const tc_handle* h, uint32_t rank, uint32_t chunk, uint32_t count,
+            void* stream) {
+  if (!P || !h) return fail(TC_EINVAL, "mark: NULL argument");
+  if (rank >= P->P || chunk >= P->chunk_base[rank + 1] - P->chunk_base[rank])
+    return fail(TC_EINVAL, "mark: no such (rank, chunk)");
+  if (count == 0) return TC_OK;
+  MarkArgs a{};
+  a.h = *h;
+  a.rank = rank;
+  a.chunk = chunk;
+  hipLaunchKernelGGL(mark_kernel, dim3(count), dim3(64), 0, (hipStream_t)stream, a);
+  TC_HIP(hipGetLastError());
+  return TC_OK;
+}
+
+int tc_consume_copy(tc_plan* P, const tc_handle* h, uint32_t dst, void* out_buf,
+                    uint32_t max_polls, uint32_t* status, void* stream) {
+  if (!P || !h || !out_buf || !status) return fail(TC_EINVAL, "consume: NULL argument");
+  if (dst >= P->P) return fail(TC_EINVAL, "consume: dst out of range");
+  if (P->G == 0) return TC_OK;
+  ConsumeArgs a{};
+  a.h = *h;
+  a.rep_dst = (uint64_t)P->rep[dst];
+  a.out = (uint8_t*)out_buf;
+  a.pieces = reinterpret_cast<const tc::PieceD*>(P->ws + P->L.pieces);
+  a.chunks = reinterpret_cast<const tc::ChunkD*>(P->ws + P->L.chunks);
+  a.status = status;
+  a.dst = dst;
+  a.max_polls = max_polls;
+  hipLaunchKernelGGL(consume_kernel, dim3(P->G), dim3(256), 0, (hipStream_t)stream, a);
+  TC_HIP(hipGetLastError());
+  return TC_OK;
+}
+
+}  // extern "C"
