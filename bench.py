@@ -1,0 +1,326 @@
+#!/usr/bin/env python
+"""Benchmark of the triggered chunked all-gather on one MI355X.
+
+A step is one round of the whole path on the 4-rank x 1.5 GiB workload
+(per-rank u32 [786432, 512], three 0.5 GiB row-block chunks, 64 writers
+each): the producer writes every rank's block, the round starts, the
+writers' marks open the gates, the copy engine delivers every chunk to the
+three other replicas and signals its arrivals, wait() checks completion,
+next_round() re-arms.  Marks are deferred (issued by a mark kernel after the
+fill), so the copy engine's window holds no producer traffic.
+
+Printed: one JSON line.  `value` = delivered bytes per step (P(P-1)S) / step
+time.  `roofline` = the copy-engine kernel: algorithmic HBM bytes per launch
+(P^2 S: every source byte read once, written P-1 times) / its mean launch
+time from HIP events on the engine's stream.  Extras: the GEMM producer's
+slowdown when the engine overlaps it, barrier and small-round latencies,
+and the CPU oracle on a bounded sample.
+"""
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "delivered all-gather GB/s and % of HBM peak; producer overlap slowdown %"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def rank_setup(w, torch, tc):
+    e = {"u32": 4, "bf16": 2, "u8": 1}[w["elem"]]
+    P, rows, cols = w["P"], w["rows"], w["cols"]
+    B = P * rows * cols * e
+    views = [tc.View(p * rows * cols * e, rows, cols, cols, e, 0) for p in range(P)]
+    rep = torch.full((P, B), 0xA5, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()       # producers run on other streams
+    return views, rep, B
+
+
+def build_sched(w, views, tc):
+    if w["builder"] == "whole":
+        return [tc.whole(v, w["writers"]) for v in views]
+    if w["builder"] == "chunks":
+        return [tc.chunks(v, w["n"], w["writers"]) for v in views]
+    tm, tn = -(-w["rows"] // w["bm"]), -(-w["cols"] // w["bn"])
+    order = tc.order_grouped(tm, tn, w["group_m"]) if w.get("group_m") else None
+    return [tc.tile_chunks(v, (w["bm"], w["bn"]), w["tiles_per_chunk"], order=order) for v in views]
+
+
+def run_headline(args, torch, tc, workloads, seed):
+    w = workloads.FULL[args.workload]
+    P = w["P"]
+    views, rep, B = rank_setup(w, torch, tc)
+    S = B // P
+    scheds = build_sched(w, views, tc)
+    plan = tc.TriggeredPlan(rep, scheds, engine_ctas=args.engine_ctas, piece_bytes=args.piece_bytes)
+    prod = torch.cuda.Stream()
+    engine_ms, window_ticks = [], []
+
+    def step(record):
+        h = plan.current_handle()
+        plan.fill(h, views, seed, kind=w["elem"], mark=False, stream=prod)
+        plan.start(prod)
+        plan.mark_all(h, stream=prod)
+        plan.wait(60.0)
+        if record:
+            st = plan.stats()
+            engine_ms.append(st["engine_ms"])
+            window_ticks.append(st["window_ticks"])
+        plan.next_round()
+
+    log(f"headline {args.workload}: P={P}, {S / 2**30:.2f} GiB per rank, warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    st = plan.stats()
+    delivered = P * (P - 1) * S
+    algo_bytes = P * P * S
+    eng = statistics.mean(engine_ms)
+    achieved = algo_bytes / (eng * 1e-3) / 1e9
+    out = dict(ms_per_step=ms_per_step, value=delivered / (ms_per_step * 1e-3) / 1e9,
+               engine_ms_mean=eng, engine_ms_median=statistics.median(engine_ms),
+               engine_ms_min=min(engine_ms), achieved=achieved,
+               window_ms_median=statistics.median(window_ticks) / 1e5,
+               engine_ctas=st["engine_ctas"], pieces=st["pieces"],
+               delivered=delivered, algo_bytes=algo_bytes, S=S, P=P, w=w)
+
+    # Full triggered rounds: the fill marks each chunk as its writers finish,
+    # so copies overlap the production of later chunks.
+    if not args.no_extras:
+        times = []
+        for i in range(max(3, args.steps // 4)):
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            h = plan.start(prod)
+            plan.fill(h, views, seed, kind=w["elem"], mark=True, stream=prod)
+            plan.wait(60.0)
+            plan.next_round()
+            times.append(time.perf_counter() - a)
+        out["overlapped_round_ms"] = statistics.median(times) * 1e3
+        out["overlapped_delivered_gbs"] = delivered / statistics.median(times) / 1e9
+    plan.close()
+    del rep
+    torch.cuda.empty_cache()
+    return out
+
+
+def run_overlap(torch, tc, workloads, seed, reps=15, cu_mask=None, engine_ctas=0):
+    """GEMM producer time for P ranks back to back, without any plan and with
+    the copy engine delivering each rank's tiles while the next GEMM runs."""
+    from synth import gemm_operands
+    import numpy as np
+    w = workloads.FULL["gemm_tiles_p4"]
+    P, M, N, K = w["P"], w["rows"], w["cols"], w["K"]
+    views, rep, B = rank_setup(w, torch, tc)
+    ops = []
+    for p in range(P):
+        a, bt = gemm_operands(seed, p, 1, M, N, K)
+        ops.append((torch.from_numpy(a.view(np.int16)).cuda(), torch.from_numpy(bt.view(np.int16)).cuda()))
+    prod = torch.cuda.Stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def gemms(h):
+        for p in range(P):
+            tc.gemm_bf16(ops[p][0], ops[p][1], rep[p][p * M * N * 2:], ldc=N, M=M, N=N,
+                         programs=w["programs"], group_m=w["group_m"], handle=h, rank=p,
+                         first_chunk=0, tiles_per_chunk=w["tiles_per_chunk"], stream=prod)
+
+    alone = []
+    for i in range(reps + 2):
+        torch.cuda.synchronize()
+        e0.record(prod)
+        gemms(None)
+        e1.record(prod)
+        e1.synchronize()
+        if i >= 2:
+            alone.append(e0.elapsed_time(e1))
+    plan = tc.TriggeredPlan(rep, build_sched(w, views, tc), cu_mask=cu_mask, engine_ctas=engine_ctas)
+    over, rounds = [], []
+    for i in range(reps + 2):
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        h = plan.start(prod)
+        e0.record(prod)
+        gemms(h)
+        e1.record(prod)
+        plan.wait(30.0)
+        plan.next_round()
+        b = time.perf_counter()
+        if i >= 2:
+            over.append(e0.elapsed_time(e1))
+            rounds.append((b - a) * 1e3)
+    plan.close()
+    flops = 2.0 * M * N * K * P
+    ma, mo = statistics.median(alone), statistics.median(over)
+    return dict(gemm_ms_alone=ma, gemm_ms_overlapped=mo, slowdown_pct=(mo / ma - 1) * 100,
+                gemm_tflops_alone=flops / (ma * 1e-3) / 1e12,
+                mfma_frac_alone=flops / (ma * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                round_ms=statistics.median(rounds),
+                delivered_gbs=P * (P - 1) * (B // P) / (statistics.median(rounds) * 1e-3) / 1e9)
+
+
+def run_barrier(torch, tc, workloads):
+    w = workloads.FULL["barrier_p8"]
+    P, G = w["P"], w["gens"]
+    W = torch.zeros((P, P), dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    first, res = 1, []
+    for i in range(4):
+        e0.record(s)
+        tc.barrier(W, P, first, G, status, stream=s)
+        e1.record(s)
+        e1.synchronize()
+        first += G
+        if i:
+            res.append(e0.elapsed_time(e1) * 1e3 / G)
+    assert int(status.item()) == 0
+    return dict(us_per_generation=statistics.median(res), P=P, generations=G)
+
+
+def run_small_round(torch, tc, workloads, seed, name, rounds):
+    w = workloads.FULL[name]
+    views, rep, B = rank_setup(w, torch, tc)
+    plan = tc.TriggeredPlan(rep, build_sched(w, views, tc))
+    prod = torch.cuda.Stream()
+    times = []
+    for i in range(rounds + 5):
+        a = time.perf_counter()
+        h = plan.start(prod)
+        plan.fill(h, views, seed, kind=w["elem"], mark=True, stream=prod)
+        plan.wait(30.0)
+        plan.next_round()
+        if i >= 5:
+            times.append((time.perf_counter() - a) * 1e6)
+    plan.close()
+    P = w["P"]
+    med = statistics.median(times)
+    return dict(us_per_round_median=med, us_p10=sorted(times)[len(times) // 10],
+                us_p90=sorted(times)[9 * len(times) // 10],
+                delivered_gbs=P * (P - 1) * (B // P) / (med * 1e-6) / 1e9)
+
+
+def cpu_baseline(workloads, seed, budget_s=12.0):
+    """The oracle, as it stands, on a bounded sample of the headline workload:
+    the same P, chunking and writers with 1/96 of the rows per rank."""
+    import numpy as np
+    from oracle import plan as oplan
+    from oracle import schedule as osched
+    from oracle import values as ovalues
+    w = workloads.FULL["u32_chunks_1p5g_p4"]
+    P, cols = w["P"], w["cols"]
+    rows = w["rows"] // 96
+    nb = rows * cols * 4
+    ov = [osched.View(p * nb, rows, cols, cols, 4) for p in range(P)]
+    reps = [np.full(P * nb, 0xA5, dtype=np.uint8) for _ in range(P)]
+    sim = oplan.PlanSim(reps, [osched.chunks(v, w["n"], w["writers"]) for v in ov])
+
+    def produce(p, r):
+        sim.rep[p][p * nb:(p + 1) * nb] = ovalues.block_bytes("u32", seed, p, r, rows * cols)
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        oplan.run_round(sim, produce)
+        sim.next_round()
+        n += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = (time.perf_counter() - t0) / n
+    return {"value": P * (P - 1) * nb / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"P={P}, {rows}x{cols} u32 per rank ({nb / 2**20:.0f} MiB, 1/96 of the rows), "
+                      f"chunks({w['n']}), {w['writers']} writers, {n} full oracle rounds "
+                      f"(produce + marks + in-order copies + wait) in {dt * n:.1f} s on one core"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="u32_chunks_1p5g_p4")
+    ap.add_argument("--engine-ctas", type=int, default=0)
+    ap.add_argument("--piece-bytes", type=int, default=0)
+    ap.add_argument("--overlap-engine-ctas", type=int, default=0)
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the P ranks of the "
+              "all-gather are simulated as P replicas in one GPU's HBM.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import triggered_copy_amd as tc
+    from synth import BASE_SEED, workloads
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    tc.lib()
+
+    h = run_headline(args, torch, tc, workloads, BASE_SEED)
+    w = h["w"]
+    extras = {}
+    if not args.no_extras:
+        log("overlap: 4 GEMM producers with and without the copy engine")
+        extras["gemm_overlap"] = run_overlap(torch, tc, workloads, BASE_SEED,
+                                             engine_ctas=args.overlap_engine_ctas)
+        log("barrier: 8 ranks x 1000 generations")
+        extras["barrier_p8"] = run_barrier(torch, tc, workloads)
+        log("small rounds")
+        extras["bf16_chunks_p2_round"] = run_small_round(torch, tc, workloads, BASE_SEED, "bf16_chunks_p2", 200)
+        extras["u32_whole_p8_round"] = run_small_round(torch, tc, workloads, BASE_SEED, "u32_whole_p8", 50)
+        extras["overlapped_triggered_round"] = {"ms": h.get("overlapped_round_ms"),
+                                                "delivered_gbs": h.get("overlapped_delivered_gbs")}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: the oracle on a bounded sample")
+        cpu = cpu_baseline(workloads, BASE_SEED)
+    line = {
+        "metric": METRIC,
+        "value": round(h["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(h["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "P": w["P"], "bytes_per_rank": h["S"],
+                   "builder": w["builder"], "chunks": w.get("n", 1), "writers": w["writers"],
+                   "marks": "deferred (fill, start, mark kernel)",
+                   "engine_ctas": h["engine_ctas"], "pieces_per_round": h["pieces"]},
+        "roofline": {"bound": "hbm", "achieved": round(h["achieved"], 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(h["achieved"] / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "kernel": "engine_kernel", "algo_bytes_per_launch": h["algo_bytes"],
+                     "launch_ms_mean": round(h["engine_ms_mean"], 4)},
+        "hbm_frac": round(h["achieved"] / HBM_PEAK_GBS, 4),
+        "engine_window_ms_median": round(h["window_ms_median"], 4),
+        "overlap_slowdown_pct": round(extras["gemm_overlap"]["slowdown_pct"], 2) if extras else None,
+        "cpu_baseline": cpu,
+        "extras": extras,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -192,8 +192,8 @@ typedef struct tc_plan_desc {
   uint64_t rows_per_rank_bytes;        /* for TC_CHECK_OWN_ROWS */
   const uint32_t* cu_mask;             /* NULL = copy engine may use every CU */
   uint32_t cu_mask_words;
-  uint32_t engine_ctas;                /* 0 = library default */
-  uint64_t piece_bytes;                /* copy work unit; 0 = library default */
+  uint32_t engine_ctas;                /* CTAs of 4 worker waves; 0 = 4 per usable CU */
+  uint64_t piece_bytes;                /* copy work unit, multiple of 256, <= 1 GiB; 0 = 8 KiB */
   uint64_t engine_backstop_us;         /* engine gives up after this long; 0 = 30 s */
 } tc_plan_desc;
 
@@ -232,6 +232,11 @@ int tc_plan_create(const tc_plan_desc* desc, tc_plan** out);
  * whole device (the engine is waiting for that producer).
  * TC_ESTATE unless READY; TC_EINVAL for the legacy default stream. */
 int tc_plan_start(tc_plan* plan, void* stream, tc_handle* out);
+
+/* The current round's handle without starting the round (state READY or
+ * STARTED): for producers that write their data before start() and mark it
+ * after (the deferred-mark mode of tc_produce_fill / tc_mark_all). */
+int tc_plan_handle(const tc_plan* plan, tc_handle* out);
 
 /* Blocks until every chunk is delivered everywhere ([TP] Model: wait()):
  * waits for the copy engine and for the work queued so far on start()'s
@@ -316,8 +321,10 @@ typedef struct tc_fill_desc {
 } tc_fill_desc;
 
 /* Hash-fill producer for every rank's chunks of `plan`, on `stream`.
- * Writes replica p only (rank p's regions).  TC_EINVAL on a kind / view /
- * order mismatch. */
+ * Writes replica p only (rank p's regions).  With TC_MARK_INKERNEL the plan
+ * must be STARTED; with TC_MARK_NONE it may also be READY (data written
+ * before start(), marked after it).  TC_EINVAL on a kind / view / order
+ * mismatch; TC_ESTATE when h is not the plan's current round. */
 int tc_produce_fill(tc_plan* plan, const tc_handle* h, const tc_fill_desc* d, void* stream);
 
 /* Deferred marks: every chunk of every rank receives exactly its writers'

@@ -10,8 +10,8 @@
  * store itself needs no release: it follows the releasing increment.
  *
  * Consumer side (same section; [TP] The kernel author's contract, item 5):
- * arrived/wait read the arrival counter with an acquire at system scope.  One
- * thread reads, the CTA barrier hands the result to every wave, and polling
+ * arrived/wait read the arrival counter, then acquire at system scope.  One
+ * wave reads, the CTA barrier hands the result to every wave, and polling
  * loops count polls instead of reading a clock, so every wave takes the same
  * exit.  All tc_mark_ready / tc_arrived / tc_wait calls are whole-CTA calls:
  * every thread of the CTA must make them, outside divergent branches.
@@ -46,7 +46,36 @@ __device__ inline bool tc_is_cta_leader() {
   return threadIdx.x == 0 && threadIdx.y == 0 && threadIdx.z == 0;
 }
 
-/* mark_ready(chunk) by one writer CTA of rank `rank`.  Whole CTA. */
+/* Linear thread id in the CTA; threads 0..63 form wave 0. */
+__device__ inline uint32_t tc_linear_tid() {
+  return threadIdx.x + blockDim.x * (threadIdx.y + blockDim.y * threadIdx.z);
+}
+
+/* Lane index within the 64-lane wave. */
+__device__ inline uint32_t tc_lane_id() {
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+/* A value read back as a wave-uniform scalar (the first active lane's).
+ * Branches on it are scalar branches.  Code in these headers never branches
+ * per lane inside a loop that synchronizes: a loop exit or a leader-only
+ * block that the compiler must treat as per-lane may be lowered so that one
+ * lane leaves the loop while the rest of its wave keeps iterating, which
+ * deadlocks against barriers or cross-lane reads.  Leader work is therefore
+ * done by a whole wave, with lane-specific values chosen by select, except
+ * where a single-lane block holds no loop and ends at a barrier. */
+__device__ inline uint32_t tc_uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline uint64_t tc_uniform64(uint64_t v) {
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+/* mark_ready(chunk) by one writer CTA of rank `rank`.  Whole CTA.  The
+ * leader thread alone does the increment: a 64-bit release atomic issued by a
+ * whole wave would be 64 serialized atomics.  The leader block holds no loop
+ * and is followed by the closing barrier, so it cannot be merged into a
+ * caller's loop back-edge. */
 __device__ inline void tc_mark_ready(const tc_handle& h, uint32_t rank, uint32_t chunk) {
   __builtin_amdgcn_s_waitcnt(TC_WAITCNT_VMCNT0);  // this wave's stores are done
   __syncthreads();                                // ... and so are every other wave's
@@ -63,23 +92,29 @@ __device__ inline void tc_mark_ready(const tc_handle& h, uint32_t rank, uint32_t
   __syncthreads();
 }
 
-/* One acquire poll of chunk (src, chunk) as seen by rank dst.  Leader only. */
+/* One relaxed poll of chunk (src, chunk) as seen by rank dst, wave-uniform:
+ * every lane reads the same word.  The caller acquires after a true result. */
 __device__ inline bool tc_poll_once(const tc_handle& h, uint32_t dst, uint32_t src,
                                     uint32_t chunk) {
   tc_gate_row* row = tc_gate_row_ptr(h, dst, src, chunk);
   const uint64_t* field = (dst == src) ? &row->ready : &row->arrival;
-  const uint32_t lo = (uint32_t)__hip_atomic_load(field, __ATOMIC_ACQUIRE,
-                                                  __HIP_MEMORY_SCOPE_SYSTEM);
+  const uint32_t lo = tc_uniform(
+      (uint32_t)__hip_atomic_load(field, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM));
   return lo >= h.round;
 }
 
 /* arrived(chunk): has rank src's chunk of this round arrived at rank dst?
- * One atomic; the result reaches every wave through the CTA barrier. */
+ * Wave 0 reads the arrival word once; the result reaches every wave through
+ * the CTA barrier.  Data read after a true return is this round's. */
 __device__ inline bool tc_arrived(const tc_handle& h, uint32_t dst, uint32_t src, uint32_t chunk) {
   __shared__ uint32_t tc_flag;
-  if (tc_is_cta_leader()) tc_flag = tc_poll_once(h, dst, src, chunk) ? 1u : 0u;
+  if (tc_linear_tid() < 64) {
+    const bool ok = tc_poll_once(h, dst, src, chunk);
+    if (ok) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");  // system-scope acquire
+    tc_flag = ok ? 1u : 0u;
+  }
   __syncthreads();
-  const bool ok = tc_flag != 0;
+  const bool ok = tc_uniform(tc_flag) != 0;
   __syncthreads();
   return ok;
 }
@@ -89,16 +124,20 @@ __device__ inline bool tc_arrived(const tc_handle& h, uint32_t dst, uint32_t src
 __device__ inline bool tc_wait(const tc_handle& h, uint32_t dst, uint32_t src, uint32_t chunk,
                                uint32_t max_polls) {
   __shared__ uint32_t tc_flag;
-  if (tc_is_cta_leader()) {
+  if (tc_linear_tid() < 64) {
     uint32_t ok = 0;
     for (uint32_t i = 0; i < max_polls; ++i) {
-      if (tc_poll_once(h, dst, src, chunk)) { ok = 1; break; }
+      if (tc_poll_once(h, dst, src, chunk)) {
+        ok = 1;
+        break;
+      }
       __builtin_amdgcn_s_sleep(2);
     }
+    if (ok) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");    // system-scope acquire
     tc_flag = ok;
   }
   __syncthreads();
-  const bool ok = tc_flag != 0;
+  const bool ok = tc_uniform(tc_flag) != 0;
   __syncthreads();
   return ok;
 }

@@ -104,6 +104,7 @@ class Pair:
         else:
             self.sim = oplan.PlanSim(None, self.os, buffer_bytes=self.B)
         self.stream = torch.cuda.Stream()     # the producers' stream (not the legacy default)
+        torch.cuda.synchronize()              # the sentinel fill ran on the default stream
 
     def oracle_round(self, mark_order=None, extra=(), withheld=()):
         w = self.w

@@ -306,6 +306,13 @@ class TriggeredPlan:
         self.handle = h
         return h
 
+    def current_handle(self) -> Handle:
+        """This round's handle without starting it (for data written before
+        start() and marked after it)."""
+        h = Handle()
+        _check(lib().tc_plan_handle(self._p, C.byref(h)))
+        return h
+
     def wait(self, timeout_s: float = 30.0):
         rc = lib().tc_plan_wait(self._p, int(timeout_s * 1e6))
         if rc in (_lib.ETIMEOUT, _lib.EEXTRA, _lib.ECORRUPT):

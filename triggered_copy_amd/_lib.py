@@ -71,6 +71,7 @@ _SIGS = {
     "tc_plan_create": [C.POINTER(PlanDesc), C.POINTER(vp)],
     "tc_plan_start": [vp, vp, C.POINTER(Handle)],
     "tc_plan_wait": [vp, u64],
+    "tc_plan_handle": [vp, C.POINTER(Handle)],
     "tc_plan_next_round": [vp],
     "tc_plan_close": [vp],
     "tc_plan_state": [vp, C.POINTER(C.c_int), C.POINTER(u32)],

@@ -56,7 +56,7 @@ void build_pieces(uint32_t nranks, const tc_schedule* const* sched, uint64_t pie
                   std::vector<PieceD>& pieces, std::vector<ChunkD>& chunks,
                   std::vector<uint32_t>& piece_base, std::vector<uint32_t>& chunk_base);
 
-constexpr uint64_t kDefaultPieceBytes = 256ull << 10;
+constexpr uint64_t kDefaultPieceBytes = 8ull << 10;
 
 inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 

@@ -5,24 +5,29 @@
 // Plans" (Iris pull request).
 //
 // The pages' copy engine is a DMA engine fed, per peer, one in-order queue of
-// "poll the chunk's gate >= round, copy each region, add 1 to the peer's
-// arrival counter" chains ([TP] opening diagram; [PR] Design notes).  Here
+// chains: poll the chunk's gate against the round, copy each region, add 1 to
+// the peer's arrival counter ([TP] opening diagram; [PR] Design notes).  Here
 // the engine is a persistent kernel on the same GPU:
 //
 //  * Work units ("pieces") are whole rows of one region, about piece_bytes
-//    each, listed per source rank in schedule order.  CTAs claim pieces of a
-//    source with an atomic ticket, so the pieces of one chunk spread over many
-//    CUs while claims stay in schedule order.
-//  * A CTA reading a chunk for the first time polls its gate (low 32 bits of
-//    `ready` >= round) and then acquires at system scope, so the chunk's data
-//    is read after the producer's release.
+//    each (8 KiB by default), listed per source rank in schedule order.  Every
+//    64-lane wave is an independent worker that claims pieces of a source
+//    with an atomic ticket, so consecutive pieces are in flight on different
+//    CUs at once and the addresses in flight stay within a narrow window.
+//  * A wave reading a chunk for the first time polls its gate (low 32 bits of
+//    `ready` >= round).  Data is read with device-scope loads, which return
+//    the coherent copy, so no cache invalidate is needed after the gate.
 //  * A piece is read once and written to all P-1 other replicas (fan-out): the
 //    P per-peer queues of one source see the same gates, so they advance
 //    together and delivering to all of them at once changes no outcome.
-//  * The CTA finishing a chunk's last piece signals it: it waits until every
+//    Stores are system-scope write-through, so once the wave's store counter
+//    drains the bytes are visible without an L2 write-back.
+//  * The wave finishing a chunk's last piece signals it: it waits until every
 //    earlier chunk of the same source has been signalled (head-of-line order,
-//    [TP] contract item 1), releases, adds 1 to `arrival` in every receiver's
-//    gate row, and advances the queue cursors.
+//    [TP] contract item 1), adds 1 to `arrival` in every receiver's gate row,
+//    and advances the queue cursors.
+//  * All control flow is wave-uniform; lanes past the end of a piece are
+//    masked by the buffer range check.
 //
 // Every poll loop also watches an abort word in pinned host memory and a
 // wall-clock backstop, so every wave of the engine exits even when a gate
@@ -64,7 +69,9 @@ Layout compute_layout(uint32_t P, uint32_t G, uint64_t npieces) {
   L.chunks = take((uint64_t)G * sizeof(ChunkD));
   L.writers = take((uint64_t)G * 4);
   L.wprefix = take((uint64_t)(G + 1) * 8);
-  L.launch_bytes = align_up((uint64_t)P * kTicketStride * 4 + kStatsWords * 8 + (uint64_t)G * 4, 256);
+  // tickets (one line per source) | stats | stop word | done (one line per chunk)
+  L.launch_bytes = align_up((uint64_t)P * kTicketStride * 4 + kStatsWords * 8 + 128 +
+                                (uint64_t)G * kTicketStride * 4, 256);
   L.launch[0] = take(L.launch_bytes);
   L.launch[1] = take(L.launch_bytes);
   L.round_bytes = align_up((uint64_t)P * kTicketStride * 4 + (uint64_t)P * P * 4, 256);
@@ -88,9 +95,17 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kEngineThreads = 256;
-constexpr int kUnroll = 8;
-constexpr uint32_t kStopCheckEvery = 64;
+constexpr int kEngineThreads = 256;     // 4 independent waves per CTA
+constexpr int kUnroll = 2;              // 16-byte vectors in flight per lane per step
+constexpr int kBufWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
+// Cache policy of the engine's buffer accesses: loads at device scope (sc1)
+// read the coherent copy, so no L2 invalidate is needed after a gate opens;
+// stores at system scope (sc0 sc1) are written through, so their completion
+// (vmcnt) already means "visible", and no L2 write-back is needed before an
+// arrival is signalled.
+constexpr int kLoadPolicy = 16;
+constexpr int kStorePolicy = 17;
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;  // offset past every buffer: access dropped
 
 struct EngineArgs {
   uint64_t rep[TC_MAX_RANKS];
@@ -99,8 +114,9 @@ struct EngineArgs {
   uint8_t* gates;
   uint64_t gate_stride;
   uint32_t* tickets;      // this launch: one per source, kTicketStride apart
-  uint32_t* done;         // this launch: pieces finished, per chunk
+  uint32_t* done;         // this launch: pieces finished, per chunk, kTicketStride apart
   uint64_t* stats;        // this launch: [0] ~first gate seen, [1] last signal
+  uint32_t* stop;         // this launch: set once any wave saw the abort or backstop
   uint32_t* zero_launch;  // the other launch block, cleared for the next launch
   uint32_t zero_launch_words;
   uint32_t zero_round_words;
@@ -119,33 +135,71 @@ struct EngineArgs {
 
 __device__ inline uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
 
-// Leader only: true when this launch must give up (host abort or backstop).
-__device__ inline bool must_stop(const EngineArgs& a, uint64_t t0) {
-  const uint32_t ab = __hip_atomic_load(a.abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  if (ab >= a.launch_id) {
-    __hip_atomic_fetch_or(a.status, kStatusAborted, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    return true;
-  }
-  if (now_ticks() - t0 > a.backstop_ticks) {
-    __hip_atomic_fetch_or(a.status, kStatusExpired, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    return true;
-  }
-  return false;
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufWord3);
 }
 
-// Leader only: spin until the u32 at `word` is >= target, then acquire.
+// Whole-wave atomic add where only lane 0 contributes `v`; every lane gets
+// lane 0's old value.  Device (agent) scope: the engine's own counters are
+// only ever read on this GPU.
+__device__ inline uint32_t wave_add(uint32_t* p, uint32_t v) {
+  const uint32_t mine = tc_lane_id() == 0 ? v : 0u;
+  return tc_uniform(__hip_atomic_fetch_add(p, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ inline uint32_t wave_load(const uint32_t* p) {
+  return tc_uniform(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+// Gates, the abort word and the cursors are shared with the host and with
+// other kernels: system scope.
+__device__ inline uint32_t wave_load_sys(const uint32_t* p) {
+  return tc_uniform(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM));
+}
+__device__ inline void wave_max64(uint64_t* p, uint64_t v) {
+  const uint64_t mine = tc_lane_id() == 0 ? v : 0u;
+  __hip_atomic_fetch_max(p, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void wave_wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// True when this launch must give up.  Uniform.  Checked every 16 spins:
+// the device stop word (cheap) and the backstop clock; every 512 spins (about
+// 1.5 ms of waiting) the waiting wave also reads the host's abort word (a
+// PCIe read) and, when it is set, raises the stop word for all.
+__device__ inline bool must_stop(const EngineArgs& a, uint64_t t0, uint32_t spins) {
+  if (spins % 16 != 0) return false;
+  if (wave_load(a.stop) != 0) return true;
+  uint32_t flag = 0;
+  if (now_ticks() - t0 > a.backstop_ticks) flag = kStatusExpired;
+  else if (spins % 512 == 0 && wave_load_sys(a.abort_word) >= a.launch_id) flag = kStatusAborted;
+  if (flag == 0) return false;
+  __hip_atomic_fetch_or(a.status, tc_lane_id() == 0 ? flag : 0u, __ATOMIC_RELAXED,
+                        __HIP_MEMORY_SCOPE_SYSTEM);
+  __hip_atomic_store(a.stop, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  return true;
+}
+
+// Uniform spin until the u32 at `word` is >= target.  Waves sleep longer
+// the longer they wait; "reserve" waves (all but one in eight) sleep about
+// 20 us between polls once they have waited a little, so thousands of idle
+// workers put almost no load on the memory system while a producer runs.
 __device__ inline bool poll_ge(const EngineArgs& a, const uint32_t* word, uint32_t target,
-                               uint64_t t0, uint32_t* seen) {
+                               uint64_t t0, bool reserve, uint32_t* seen) {
   uint32_t spins = 0;
   for (;;) {
-    const uint32_t v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const uint32_t v = wave_load_sys(word);
     if (v >= target) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
       if (seen) *seen = v;
+      asm volatile("" ::: "memory");  // no later access is moved above the poll
       return true;
     }
-    if (++spins % kStopCheckEvery == 0 && must_stop(a, t0)) return false;
-    __builtin_amdgcn_s_sleep(1);
+    if (must_stop(a, t0, ++spins)) return false;
+    if (spins < 8) {
+      __builtin_amdgcn_s_sleep(2);
+    } else if (!reserve) {
+      if (spins < 64) __builtin_amdgcn_s_sleep(16);
+      else __builtin_amdgcn_s_sleep(64);
+    } else {
+      for (int k = 0; k < 6; ++k) __builtin_amdgcn_s_sleep(127);
+    }
   }
 }
 
@@ -154,165 +208,155 @@ __device__ inline tc_gate_row* gate_row(const EngineArgs& a, uint32_t table, uin
                                         (uint64_t)g * TC_GATE_ROW_BYTES);
 }
 
-// Leader only: signal chunk `c` (global id g) of source p once every earlier
-// chunk of p has been signalled.
+// Signal chunk `c` (global id g) of source p once every earlier chunk of p
+// has been signalled.  Every piece's stores completed (at system scope)
+// before its `done` increment, so the bytes are visible when this runs.
 __device__ bool signal_in_order(const EngineArgs& a, uint32_t p, uint32_t c, uint32_t g,
                                 uint64_t t0) {
   uint32_t* sig = a.sig + p * kTicketStride;
   uint32_t seen = 0;
-  if (!poll_ge(a, sig, c, t0, &seen)) return false;
+  if (!poll_ge(a, sig, c, t0, false, &seen)) return false;
   if (seen > c) return true;  // signalled by an earlier launch of this round
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");  // every piece's bytes are in memory
-  for (uint32_t q = 0; q < a.nranks; ++q) {
-    if (q == p) continue;
-    __hip_atomic_fetch_add(&gate_row(a, q, g)->arrival, (uint64_t)1, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_SYSTEM);
-    __hip_atomic_store(a.cur + p * a.nranks + q, c + 1, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_SYSTEM);
-  }
-  __hip_atomic_fetch_max(&a.stats[1], now_ticks(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(sig, c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  const uint64_t one = tc_lane_id() == 0 ? 1u : 0u;
+  for (uint32_t q = 0; q < a.nranks; ++q)
+    if (q != p)
+      __hip_atomic_fetch_add(&gate_row(a, q, g)->arrival, one, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_SYSTEM);
+  wave_wait_stores();  // arrivals land before the cursors and the signal count move
+  for (uint32_t q = 0; q < a.nranks; ++q)
+    if (q != p)
+      __hip_atomic_store(a.cur + p * a.nranks + q, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  wave_max64(&a.stats[1], now_ticks());
+  wave_wait_stores();
+  __hip_atomic_store(sig, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   return true;
 }
 
-// Whole CTA: copy `len` bytes at `off` of replica p to every other replica.
-__device__ void copy_linear(const EngineArgs& a, uint32_t p, uint64_t off, uint64_t len) {
-  const uint32_t tid = threadIdx.x;
+// Whole wave: copy `len` bytes at `off` of replica p to every other replica.
+// Lanes past the end are masked by the buffer range check, not by branches.
+__device__ void copy_linear(const EngineArgs& a, uint32_t p, uint64_t off, uint32_t len) {
+  const uint32_t lane = tc_lane_id();
   const uint8_t* src = reinterpret_cast<const uint8_t*>(a.rep[p]);
-  uint64_t head = (16 - (off & 15)) & 15;
+  uint32_t head = (uint32_t)((16 - (off & 15)) & 15);
   if (head > len) head = len;
-  const uint64_t body = (len - head) & ~(uint64_t)15;
-  const uint64_t tail = len - head - body;
-  if (tid < head + tail) {  // the unaligned bytes at both ends
-    const uint64_t b = tid < head ? off + tid : off + head + body + (tid - head);
-    const uint8_t v = src[b];
+  const uint32_t body = (len - head) & ~15u;
+  const uint32_t tail = len - head - body;
+  if (head + tail) {  // unaligned bytes at both ends (at most 30)
+    const __amdgpu_buffer_rsrc_t rs = rsrc(src + off, len);
+    const uint32_t o = lane < head ? lane : (lane < head + tail ? head + body + (lane - head) : kOutOfRange);
+    const uint8_t v = __builtin_amdgcn_raw_buffer_load_b8(rs, (int)o, 0, kLoadPolicy);
     for (uint32_t q = 0; q < a.nranks; ++q)
-      if (q != p) reinterpret_cast<uint8_t*>(a.rep[q])[b] = v;
+      if (q != p)
+        __builtin_amdgcn_raw_buffer_store_b8(v, rsrc(reinterpret_cast<const uint8_t*>(a.rep[q]) + off, len),
+                                             (int)o, 0, kStorePolicy);
   }
-  const uint64_t nv = body / 16;
+  if (body == 0) return;
   const uint64_t start = off + head;
-  const u32x4* s4 = reinterpret_cast<const u32x4*>(src + start);
-  for (uint64_t base = 0; base < nv; base += (uint64_t)kEngineThreads * kUnroll) {
+  const __amdgpu_buffer_rsrc_t rs = rsrc(src + start, body);
+  const uint32_t nv = body / 16;
+  for (uint32_t base = 0; base < nv; base += 64 * kUnroll) {
     u32x4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint64_t i = base + (uint64_t)u * kEngineThreads + tid;
-      if (i < nv) v[u] = __builtin_nontemporal_load(s4 + i);
-    }
+    for (int u = 0; u < kUnroll; ++u)
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)((base + u * 64 + lane) * 16), 0, kLoadPolicy);
     for (uint32_t q = 0; q < a.nranks; ++q) {
       if (q == p) continue;
-      u32x4* d4 = reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(a.rep[q]) + start);
+      const __amdgpu_buffer_rsrc_t rd = rsrc(reinterpret_cast<const uint8_t*>(a.rep[q]) + start, body);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const uint64_t i = base + (uint64_t)u * kEngineThreads + tid;
-        if (i < nv) __builtin_nontemporal_store(v[u], d4 + i);
-      }
+      for (int u = 0; u < kUnroll; ++u)
+        __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, (int)((base + u * 64 + lane) * 16), 0,
+                                               kStorePolicy);
     }
   }
 }
 
-// Whole CTA: copy a 2-D piece (rows x row_bytes at pitch).
+// Whole wave: copy a 2-D piece (rows x row_bytes at pitch; its extent fits in
+// 31 bits by construction).
 __device__ void copy_2d(const EngineArgs& a, uint32_t p, const PieceD& pc) {
-  const uint32_t tid = threadIdx.x;
-  const uint8_t* src = reinterpret_cast<const uint8_t*>(a.rep[p]);
-  const bool vec = ((pc.off | pc.pitch | pc.row_bytes) & 15) == 0;
-  if (vec) {
+  const uint32_t lane = tc_lane_id();
+  const uint32_t extent = (uint32_t)((uint64_t)(pc.rows - 1) * pc.pitch + pc.row_bytes);
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(a.rep[p]) + pc.off;
+  const __amdgpu_buffer_rsrc_t rs = rsrc(src, extent);
+  auto rd = [&](uint32_t q) {
+    return rsrc(reinterpret_cast<const uint8_t*>(a.rep[q]) + pc.off, extent);
+  };
+  const uint32_t pitch = (uint32_t)pc.pitch;
+  if (((pc.off | pc.pitch | pc.row_bytes) & 15) == 0) {
     const uint32_t vpr = pc.row_bytes / 16;
     const uint32_t nv = pc.rows * vpr;
-    for (uint32_t base = 0; base < nv; base += kEngineThreads * kUnroll) {
+    for (uint32_t base = 0; base < nv; base += 64 * kUnroll) {
       u32x4 v[kUnroll];
-      uint64_t at[kUnroll];
+      uint32_t at[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const uint32_t i = base + u * kEngineThreads + tid;
+        const uint32_t i = base + u * 64 + lane;
         const uint32_t r = i / vpr, c = i - r * vpr;
-        at[u] = pc.off + (uint64_t)r * pc.pitch + (uint64_t)c * 16;
-        if (i < nv) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + at[u]));
+        at[u] = i < nv ? r * pitch + c * 16 : kOutOfRange;
+        v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)at[u], 0, kLoadPolicy);
       }
       for (uint32_t q = 0; q < a.nranks; ++q) {
         if (q == p) continue;
-        uint8_t* dst = reinterpret_cast<uint8_t*>(a.rep[q]);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          const uint32_t i = base + u * kEngineThreads + tid;
-          if (i < nv) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(dst + at[u]));
-        }
+        for (int u = 0; u < kUnroll; ++u)
+          __builtin_amdgcn_raw_buffer_store_b128(v[u], rd(q), (int)at[u], 0, kStorePolicy);
       }
     }
   } else {
     const uint32_t n = pc.rows * pc.row_bytes;
-    for (uint32_t i = tid; i < n; i += kEngineThreads) {
+    for (uint32_t base = 0; base < n; base += 64) {
+      const uint32_t i = base + lane;
       const uint32_t r = i / pc.row_bytes, c = i - r * pc.row_bytes;
-      const uint64_t b = pc.off + (uint64_t)r * pc.pitch + c;
-      const uint8_t v = src[b];
+      const uint32_t at = i < n ? r * pitch + c : kOutOfRange;
+      const uint8_t v = __builtin_amdgcn_raw_buffer_load_b8(rs, (int)at, 0, kLoadPolicy);
       for (uint32_t q = 0; q < a.nranks; ++q)
-        if (q != p) reinterpret_cast<uint8_t*>(a.rep[q])[b] = v;
+        if (q != p) __builtin_amdgcn_raw_buffer_store_b8(v, rd(q), (int)at, 0, kStorePolicy);
     }
   }
 }
 
+// The copy engine.  Every wave is an independent worker; all control flow is
+// wave-uniform (no per-lane branch in any loop), so no lane can be left
+// behind in a loop its wave has to leave together.
 __global__ __launch_bounds__(kEngineThreads) void engine_kernel(EngineArgs a) {
-  __shared__ uint32_t s_word;
-  __shared__ uint32_t s_ok;
-  const uint32_t tid = threadIdx.x;
+  const uint32_t gw = tc_uniform((blockIdx.x * kEngineThreads + threadIdx.x) >> 6);
 
   // Clear the blocks the next launch and the next round will use; nothing
   // touches them while this launch runs.
-  for (uint32_t i = blockIdx.x * kEngineThreads + tid; i < a.zero_launch_words;
+  for (uint32_t i = blockIdx.x * kEngineThreads + threadIdx.x; i < a.zero_launch_words;
        i += gridDim.x * kEngineThreads)
     a.zero_launch[i] = 0;
-  for (uint32_t i = blockIdx.x * kEngineThreads + tid; i < a.zero_round_words;
+  for (uint32_t i = blockIdx.x * kEngineThreads + threadIdx.x; i < a.zero_round_words;
        i += gridDim.x * kEngineThreads)
     a.zero_round[i] = 0;
 
   const uint64_t t0 = now_ticks();
-  uint32_t acquired = 0xFFFFFFFFu;  // last chunk whose gate this CTA has acquired
+  uint32_t acquired = 0xFFFFFFFFu;  // last chunk whose gate this wave has seen open
+  const bool reserve = gw % 8 != 0;
 
   for (uint32_t s = 0; s < a.nranks; ++s) {
-    const uint32_t p = (blockIdx.x + s) % a.nranks;
+    const uint32_t p = (gw + s) % a.nranks;
     const uint32_t np = a.piece_base[p + 1] - a.piece_base[p];
     if (np == 0) continue;
     for (;;) {
-      if (tid == 0) s_word = atomicAdd(a.tickets + p * kTicketStride, 1u);
-      __syncthreads();
-      const uint32_t t = s_word;
-      __syncthreads();
+      const uint32_t t = wave_add(a.tickets + p * kTicketStride, 1u);
       if (t >= np) break;
       const PieceD pc = a.pieces[a.piece_base[p] + t];
-      const ChunkD cd = a.chunks[pc.chunk];
-      if (pc.chunk != acquired) {
-        if (tid == 0) {
-          const uint32_t* ready =
-              reinterpret_cast<const uint32_t*>(&gate_row(a, p, pc.chunk)->ready);
-          const bool ok = poll_ge(a, ready, a.round, t0, nullptr);
-          if (ok)
-            __hip_atomic_fetch_max(&a.stats[0], ~now_ticks(), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-          s_ok = ok;
-        }
-        __syncthreads();
-        if (!s_ok) return;
-        acquired = pc.chunk;
+      const uint32_t g = tc_uniform(pc.chunk);
+      if (g != acquired) {
+        const uint32_t* ready = reinterpret_cast<const uint32_t*>(&gate_row(a, p, g)->ready);
+        if (!poll_ge(a, ready, a.round, t0, reserve, nullptr)) return;
+        // The wave holding a chunk's first piece records when it saw the gate open.
+        if (a.piece_base[p] + t == a.chunks[g].first_piece) wave_max64(&a.stats[0], ~now_ticks());
+        acquired = g;
       }
       if (pc.rows == 1)
         copy_linear(a, p, pc.off, pc.row_bytes);
       else
         copy_2d(a, p, pc);
-      __builtin_amdgcn_s_waitcnt(TC_WAITCNT_VMCNT0);  // this wave's stores are done
-      __syncthreads();                                // ... and every wave's
-      if (tid == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");  // write them back past this XCD's L2
-        const uint32_t old =
-            __hip_atomic_fetch_add(a.done + pc.chunk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        bool ok = true;
-        if (old + 1 == cd.npieces) {
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
-          ok = signal_in_order(a, p, cd.local, pc.chunk, t0);
-        }
-        s_ok = ok;
-      }
-      __syncthreads();
-      if (!s_ok) return;
+      wave_wait_stores();  // this piece's bytes are visible at system scope
+      const ChunkD cd = a.chunks[g];
+      const uint32_t old = wave_add(a.done + (uint64_t)g * kTicketStride, 1u);
+      if (old + 1 == cd.npieces && !signal_in_order(a, p, cd.local, g, t0)) return;
     }
   }
 }
@@ -396,7 +440,8 @@ static int launch_engine(tc_plan* P) {
   uint8_t* cur_launch = P->ws + L.launch[lb];
   a.tickets = reinterpret_cast<uint32_t*>(cur_launch);
   a.stats = reinterpret_cast<uint64_t*>(cur_launch + (uint64_t)P->P * kTicketStride * 4);
-  a.done = reinterpret_cast<uint32_t*>(cur_launch + (uint64_t)P->P * kTicketStride * 4 + kStatsWords * 8);
+  a.stop = reinterpret_cast<uint32_t*>(cur_launch + (uint64_t)P->P * kTicketStride * 4 + kStatsWords * 8);
+  a.done = reinterpret_cast<uint32_t*>(cur_launch + (uint64_t)P->P * kTicketStride * 4 + kStatsWords * 8 + 128);
   a.zero_launch = reinterpret_cast<uint32_t*>(P->ws + L.launch[lb ^ 1u]);
   a.zero_launch_words = (uint32_t)(L.launch_bytes / 4);
   const uint32_t rb = P->round & 1u;
@@ -486,8 +531,8 @@ int tc_plan_validate(const tc_plan_desc* d) {
   if (d->buffer_bytes == 0) return fail(TC_EINVAL, "buffer_bytes is 0");
   if ((d->flags & TC_CHECK_OWN_ROWS) && d->rows_per_rank_bytes == 0)
     return fail(TC_EINVAL, "TC_CHECK_OWN_ROWS needs rows_per_rank_bytes");
-  if (d->piece_bytes && (d->piece_bytes % 256 || d->piece_bytes > (1ull << 31)))
-    return fail(TC_EINVAL, "piece_bytes must be a multiple of 256 and at most 2 GiB");
+  if (d->piece_bytes && (d->piece_bytes % 256 || d->piece_bytes > (1ull << 30)))
+    return fail(TC_EINVAL, "piece_bytes must be a multiple of 256 and at most 1 GiB");
   uint64_t G = 0;
   for (uint32_t p = 0; p < d->nranks; ++p)
     if (d->schedules && d->schedules[p]) G += d->schedules[p]->chunks.size();
@@ -598,9 +643,11 @@ int tc_plan_create(const tc_plan_desc* d, tc_plan** out) {
   }
   TC_HIP_C(hipMemcpy(P->ws + P->L.wprefix, wprefix.data(), wprefix.size() * 8, hipMemcpyHostToDevice));
 
+  // Default: 4 CTAs of 4 waves per usable CU (16 worker waves per CU), but
+  // no more waves than pieces.
   const uint32_t npieces = (uint32_t)P->pieces.size();
-  P->engine_ctas = d->engine_ctas ? d->engine_ctas : 2 * usable;
-  P->engine_ctas = std::max<uint32_t>(1, std::min<uint32_t>(P->engine_ctas, std::max<uint32_t>(npieces, 1)));
+  P->engine_ctas = d->engine_ctas ? d->engine_ctas : 4 * usable;
+  P->engine_ctas = std::max<uint32_t>(1, std::min<uint32_t>(P->engine_ctas, (std::max<uint32_t>(npieces, 1) + 3) / 4));
   const uint64_t backstop_us = d->engine_backstop_us ? d->engine_backstop_us : 30ull * 1000 * 1000;
   P->backstop_ticks = backstop_us * 100;  // s_memrealtime runs at 100 MHz
   for (const ChunkD& c : P->chunks) {
@@ -696,6 +743,14 @@ int tc_plan_wait(tc_plan* P, uint64_t timeout_us) {
                                  " chunk(s) still short");
   }
   P->state = TC_STATE_DONE;
+  return TC_OK;
+}
+
+int tc_plan_handle(const tc_plan* P, tc_handle* out) {
+  if (!P || !out) return fail(TC_EINVAL, "handle: NULL argument");
+  if (P->state != TC_STATE_READY && P->state != TC_STATE_STARTED)
+    return fail(TC_ESTATE, "handle: plan is neither READY nor STARTED");
+  fill_handle(P, out);
   return TC_OK;
 }
 

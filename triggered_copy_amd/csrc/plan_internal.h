@@ -11,7 +11,7 @@
 
 namespace tc {
 
-constexpr uint32_t kTicketStride = 16;  // u32 words between per-source counters (64 B)
+constexpr uint32_t kTicketStride = 32;  // u32 words between hot counters: one 128-byte line each
 constexpr uint32_t kStatsWords = 2;     // u64 words of per-launch timestamps
 
 constexpr uint32_t kStatusAborted = 1;  // engine stopped by the host's abort word
@@ -28,7 +28,7 @@ constexpr uint32_t kFlagCorrupt = 16;    // values no correct run produces
 struct Layout {
   uint64_t gates, gate_stride;
   uint64_t pieces, chunks, writers, wprefix;
-  uint64_t launch[2], launch_bytes;     // tickets | stats | done, per launch parity
+  uint64_t launch[2], launch_bytes;     // tickets | stats | stop | done, per launch parity
   uint64_t round_blk[2], round_bytes;   // sig | cursors, per round parity
   uint64_t status;
   uint64_t check;

@@ -233,8 +233,9 @@ int tc_produce_fill(tc_plan* P, const tc_handle* h, const tc_fill_desc* d, void*
   if (!elem) return fail(TC_EINVAL, "fill: unknown kind");
   if (d->mark_mode > TC_MARK_NONE) return fail(TC_EINVAL, "fill: unknown mark mode");
   if (h->round >= (1u << 16)) return fail(TC_EINVAL, "fill: value keys hold rounds below 65536");
-  if (P->state != TC_STATE_STARTED || h->round != P->round)
-    return fail(TC_ESTATE, "fill: the handle is not this plan's started round");
+  const bool ready_ok = d->mark_mode == TC_MARK_NONE && P->state == TC_STATE_READY;
+  if ((P->state != TC_STATE_STARTED && !ready_ok) || h->round != P->round)
+    return fail(TC_ESTATE, "fill: the handle is not this plan's current round");
   FillArgs a{};
   for (uint32_t p = 0; p < P->P; ++p) {
     const tc_view& v = d->views[p];

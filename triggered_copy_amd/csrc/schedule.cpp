@@ -325,7 +325,10 @@ void tc::build_pieces(uint32_t nranks, const tc_schedule* const* sched, uint64_t
         } else if (r.row_bytes >= piece_bytes) {
           for (uint64_t row = 0; row < r.rows; ++row) linear(r.offset + row * r.pitch, r.row_bytes);
         } else {
-          const uint64_t per = std::max<uint64_t>(1, piece_bytes / r.row_bytes);
+          // Whole rows per piece; the piece's extent stays below 2^31 bytes
+          // (the engine addresses a piece with 32-bit buffer offsets).
+          const uint64_t by_extent = ((1ull << 31) - 1 - r.row_bytes) / r.pitch + 1;
+          const uint64_t per = std::max<uint64_t>(1, std::min(piece_bytes / r.row_bytes, by_extent));
           for (uint64_t row = 0; row < r.rows; row += per) {
             const uint64_t n = std::min(per, r.rows - row);
             pieces.push_back(PieceD{r.offset + row * r.pitch, r.pitch, (uint32_t)n,
