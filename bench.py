@@ -150,6 +150,21 @@ def run_overlap(torch, tc, workloads, seed, reps=15, cu_mask=None, engine_ctas=0
         e1.synchronize()
         if i >= 2:
             alone.append(e0.elapsed_time(e1))
+    # The same GEMMs marking a plan's gates with no copy engine running: the
+    # cost of the mark protocol itself (a throwaway plan whose round is never
+    # started).
+    marks_only = []
+    scratch = tc.TriggeredPlan(rep, build_sched(w, views, tc), engine_ctas=1)
+    h0 = scratch.current_handle()
+    for i in range(reps + 2):
+        torch.cuda.synchronize()
+        e0.record(prod)
+        gemms(h0)
+        e1.record(prod)
+        e1.synchronize()
+        if i >= 2:
+            marks_only.append(e0.elapsed_time(e1))
+    scratch.close()
     plan = tc.TriggeredPlan(rep, build_sched(w, views, tc), cu_mask=cu_mask, engine_ctas=engine_ctas)
     over, rounds = [], []
     for i in range(reps + 2):
@@ -165,10 +180,15 @@ def run_overlap(torch, tc, workloads, seed, reps=15, cu_mask=None, engine_ctas=0
         if i >= 2:
             over.append(e0.elapsed_time(e1))
             rounds.append((b - a) * 1e3)
+    ectas = plan.stats()["engine_ctas"]
     plan.close()
     flops = 2.0 * M * N * K * P
     ma, mo = statistics.median(alone), statistics.median(over)
-    return dict(gemm_ms_alone=ma, gemm_ms_overlapped=mo, slowdown_pct=(mo / ma - 1) * 100,
+    mm = statistics.median(marks_only)
+    return dict(gemm_ms_alone=ma, gemm_ms_marks_only=mm, gemm_ms_overlapped=mo,
+                slowdown_pct=(mo / ma - 1) * 100,
+                slowdown_vs_marks_only_pct=(mo / mm - 1) * 100,
+                mark_protocol_cost_pct=(mm / ma - 1) * 100, engine_ctas=ectas,
                 gemm_tflops_alone=flops / (ma * 1e-3) / 1e12,
                 mfma_frac_alone=flops / (ma * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                 round_ms=statistics.median(rounds),

@@ -192,7 +192,8 @@ typedef struct tc_plan_desc {
   uint64_t rows_per_rank_bytes;        /* for TC_CHECK_OWN_ROWS */
   const uint32_t* cu_mask;             /* NULL = copy engine may use every CU */
   uint32_t cu_mask_words;
-  uint32_t engine_ctas;                /* CTAs of 4 worker waves; 0 = 4 per usable CU */
+  uint32_t engine_ctas;                /* CTAs of 4 worker waves; 0 = one wave per 64 KiB of
+                                          source bytes per round, at most 16 waves per usable CU */
   uint64_t piece_bytes;                /* copy work unit, multiple of 256, <= 1 GiB; 0 = 8 KiB */
   uint64_t engine_backstop_us;         /* engine gives up after this long; 0 = 30 s */
 } tc_plan_desc;
@@ -342,8 +343,10 @@ int tc_mark(tc_plan* plan, const tc_handle* h, uint32_t rank, uint32_t chunk,
  * 128x128 tiles; program p takes steps p, p + programs, ...; step s computes
  * tile tc_tile_of(s, tm, tn, group_m) and, when h != NULL, then marks chunk
  * first_chunk + s / tiles_per_chunk of rank `rank`.  A, Bt, C device.
- * TC_EINVAL unless K % 8 == 0, N % 8 == 0, ldc % 8 == 0, pointers 16-byte
- * aligned. */
+ * C is stored with system-scope write-through stores, so the release in
+ * mark_ready has little left to write back.
+ * TC_EINVAL unless K % 8 == 0, N % 8 == 0, ldc % 8 == 0, ldc < 2^23, pointers
+ * 16-byte aligned. */
 int tc_gemm_bf16(const void* A, const void* Bt, void* C, uint32_t M, uint32_t N, uint32_t K,
                  uint64_t ldc, uint32_t programs, uint32_t group_m, const tc_handle* h,
                  uint32_t rank, uint32_t first_chunk, uint32_t tiles_per_chunk, void* stream);

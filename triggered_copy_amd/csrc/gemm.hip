@@ -144,14 +144,23 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
           lds[r * LDC + c] = (uint16_t)f32_to_bf16_rne(acc[i][j][e]);
         }
     __syncthreads();
-    // 128 rows x 16 vectors of 8 bf16: 8 vectors per thread.
+    // 128 rows x 16 vectors of 8 bf16: 8 vectors per thread, stored through
+    // to memory at system scope, so that the release in mark_ready finds
+    // nothing of this tile left to write back.  Lanes outside the matrix get
+    // an offset past the buffer range and their stores are dropped.
+    const uint32_t rows_in = a.M - m0 < (uint32_t)BM ? a.M - m0 : (uint32_t)BM;
+    const uint32_t cols_in = a.N - n0 < (uint32_t)BN ? a.N - n0 : (uint32_t)BN;
+    const uint32_t extent = (uint32_t)(((uint64_t)(rows_in - 1) * a.ldc + cols_in) * 2);
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        a.C + (uint64_t)m0 * a.ldc + n0, 0, (int)extent, 0x00020000);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const uint32_t v = tid + kThreads * s;
       const uint32_t r = v >> 4, c = (v & 15) * 8;
-      if (m0 + r < a.M && n0 + c < a.N)
-        *reinterpret_cast<u32x4*>(a.C + (uint64_t)(m0 + r) * a.ldc + n0 + c) =
-            *reinterpret_cast<const u32x4*>(lds + r * LDC + c);
+      const bool in = r < rows_in && c < cols_in;
+      const uint32_t off = in ? (uint32_t)(((uint64_t)r * a.ldc + c) * 2) : 0xFFFFFFF0u;
+      __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(lds + r * LDC + c), rc,
+                                             (int)off, 0, 17 /* sc0 sc1 */);
     }
     if (a.mark) tc_mark_ready(a.h, a.rank, a.first_chunk + step / a.tiles_per_chunk);
   }
@@ -168,6 +177,8 @@ extern "C" int tc_gemm_bf16(const void* A, const void* Bt, void* C, uint32_t M, 
     return fail(TC_EINVAL, "gemm: zero size");
   if (K % 8 || N % 8 || ldc % 8 || ldc < N)
     return fail(TC_EINVAL, "gemm: K, N and ldc must be multiples of 8 (16-byte rows), ldc >= N");
+  if ((uint64_t)BM * ldc * 2 >= (1ull << 31))
+    return fail(TC_EINVAL, "gemm: a 128-row tile of C must span less than 2 GiB (ldc < 2^23)");
   if (((uintptr_t)A | (uintptr_t)Bt | (uintptr_t)C) & 15)
     return fail(TC_EINVAL, "gemm: operands must be 16-byte aligned");
   if (h && (tiles_per_chunk == 0 || rank >= h->nranks))

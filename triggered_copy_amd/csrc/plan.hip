@@ -40,6 +40,8 @@
 #include <algorithm>
 #include <chrono>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
 #include <thread>
 #include <vector>
@@ -115,7 +117,8 @@ struct EngineArgs {
   uint64_t gate_stride;
   uint32_t* tickets;      // this launch: one per source, kTicketStride apart
   uint32_t* done;         // this launch: pieces finished, per chunk, kTicketStride apart
-  uint64_t* stats;        // this launch: [0] ~first gate seen, [1] last signal
+  uint32_t* stats;        // this launch: [0] ~first gate seen, [1] last signal (low 32 bits
+                          // of the 100 MHz clock; the window is taken modulo 2^32)
   uint32_t* stop;         // this launch: set once any wave saw the abort or backstop
   uint32_t* zero_launch;  // the other launch block, cleared for the next launch
   uint32_t zero_launch_words;
@@ -154,8 +157,10 @@ __device__ inline uint32_t wave_load(const uint32_t* p) {
 __device__ inline uint32_t wave_load_sys(const uint32_t* p) {
   return tc_uniform(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM));
 }
-__device__ inline void wave_max64(uint64_t* p, uint64_t v) {
-  const uint64_t mine = tc_lane_id() == 0 ? v : 0u;
+// 32-bit max (the compiler merges a wave's lanes into one atomic; a 64-bit
+// one would be 64 serialized atomics).
+__device__ inline void wave_max32(uint32_t* p, uint32_t v) {
+  const uint32_t mine = tc_lane_id() == 0 ? v : 0u;
   __hip_atomic_fetch_max(p, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ inline void wave_wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -218,16 +223,14 @@ __device__ bool signal_in_order(const EngineArgs& a, uint32_t p, uint32_t c, uin
   if (!poll_ge(a, sig, c, t0, false, &seen)) return false;
   if (seen > c) return true;  // signalled by an earlier launch of this round
   const uint64_t one = tc_lane_id() == 0 ? 1u : 0u;
-  for (uint32_t q = 0; q < a.nranks; ++q)
-    if (q != p)
-      __hip_atomic_fetch_add(&gate_row(a, q, g)->arrival, one, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_SYSTEM);
-  wave_wait_stores();  // arrivals land before the cursors and the signal count move
-  for (uint32_t q = 0; q < a.nranks; ++q)
-    if (q != p)
-      __hip_atomic_store(a.cur + p * a.nranks + q, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  wave_max64(&a.stats[1], now_ticks());
-  wave_wait_stores();
+  for (uint32_t q = 0; q < a.nranks; ++q) {
+    if (q == p) continue;
+    __hip_atomic_fetch_add(&gate_row(a, q, g)->arrival, one, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(a.cur + p * a.nranks + q, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+  wave_max32(&a.stats[1], (uint32_t)now_ticks());
+  wave_wait_stores();  // this chunk's arrivals land before the next chunk may signal
   __hip_atomic_store(sig, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   return true;
 }
@@ -331,7 +334,9 @@ __global__ __launch_bounds__(kEngineThreads) void engine_kernel(EngineArgs a) {
 
   const uint64_t t0 = now_ticks();
   uint32_t acquired = 0xFFFFFFFFu;  // last chunk whose gate this wave has seen open
-  const bool reserve = gw % 8 != 0;
+  // Large grids keep one wave in eight polling briskly and let the rest back
+  // off; small grids poll with every wave.
+  const bool reserve = gridDim.x >= 256 && gw % 8 != 0;
 
   for (uint32_t s = 0; s < a.nranks; ++s) {
     const uint32_t p = (gw + s) % a.nranks;
@@ -346,7 +351,7 @@ __global__ __launch_bounds__(kEngineThreads) void engine_kernel(EngineArgs a) {
         const uint32_t* ready = reinterpret_cast<const uint32_t*>(&gate_row(a, p, g)->ready);
         if (!poll_ge(a, ready, a.round, t0, reserve, nullptr)) return;
         // The wave holding a chunk's first piece records when it saw the gate open.
-        if (a.piece_base[p] + t == a.chunks[g].first_piece) wave_max64(&a.stats[0], ~now_ticks());
+        if (a.piece_base[p] + t == a.chunks[g].first_piece) wave_max32(&a.stats[0], ~(uint32_t)now_ticks());
         acquired = g;
       }
       if (pc.rows == 1)
@@ -365,7 +370,9 @@ struct CheckArgs {
   const ChunkD* chunks;
   const uint8_t* gates;
   uint64_t gate_stride;
-  uint32_t* flags;
+  uint32_t* flags;        // mapped pinned host memory, one word per chunk
+  uint32_t* status;       // device engine status word: read, reported, cleared
+  uint32_t* status_host;  // mapped pinned host memory
   uint32_t G, nranks, round, pad;
 };
 
@@ -378,6 +385,11 @@ __device__ inline uint64_t ld(const uint64_t* p) {
 // arrived at every peer).
 __global__ void check_kernel(CheckArgs a) {
   const uint32_t g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g == 0) {  // hand the engine's status to the host and clear it for the next launch
+    const uint32_t st = __hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(a.status_host, st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(a.status, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
   if (g >= a.G) return;
   const ChunkD cd = a.chunks[g];
   const uint64_t want = (uint64_t)a.round * cd.writers;
@@ -402,7 +414,7 @@ __global__ void check_kernel(CheckArgs a) {
     if (arr > a.round) f |= kFlagCorrupt;
     if (ld(&r->ready) != 0 || ld(&r->writers) != 0) f |= kFlagCorrupt;
   }
-  a.flags[g] = f;
+  __hip_atomic_store(a.flags + g, f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 }  // namespace
@@ -418,6 +430,28 @@ int hip_fail(hipError_t e, const char* what) {
     hipError_t e_ = (call);                            \
     if (e_ != hipSuccess) return hip_fail(e_, #call);  \
   } while (0)
+
+// Engine streams are shared by every plan on the same device with the same
+// CU mask and live until the process ends: each one owns a hardware queue
+// (and its wave save area), which are too costly to create per plan.  Plans
+// that share a stream run their engines in the order they were started.
+static int engine_stream_for(int device, const std::vector<uint32_t>& mask, hipStream_t* out) {
+  static std::mutex mu;
+  static std::map<std::pair<int, std::vector<uint32_t>>, hipStream_t> streams;
+  std::lock_guard<std::mutex> lock(mu);
+  auto key = std::make_pair(device, mask);
+  auto it = streams.find(key);
+  if (it != streams.end()) {
+    *out = it->second;
+    return TC_OK;
+  }
+  hipStream_t s = nullptr;
+  const hipError_t e = hipExtStreamCreateWithCUMask(&s, (uint32_t)mask.size(), mask.data());
+  if (e != hipSuccess) return hip_fail(e, "hipExtStreamCreateWithCUMask (engine stream)");
+  streams.emplace(key, s);
+  *out = s;
+  return TC_OK;
+}
 
 static int zero_device(void* p, uint64_t bytes, hipStream_t s) {
   const uint64_t words = bytes / 4;
@@ -439,7 +473,7 @@ static int launch_engine(tc_plan* P) {
   const uint32_t lb = P->launch_seq & 1u;  // launch block of this launch
   uint8_t* cur_launch = P->ws + L.launch[lb];
   a.tickets = reinterpret_cast<uint32_t*>(cur_launch);
-  a.stats = reinterpret_cast<uint64_t*>(cur_launch + (uint64_t)P->P * kTicketStride * 4);
+  a.stats = reinterpret_cast<uint32_t*>(cur_launch + (uint64_t)P->P * kTicketStride * 4);
   a.stop = reinterpret_cast<uint32_t*>(cur_launch + (uint64_t)P->P * kTicketStride * 4 + kStatsWords * 8);
   a.done = reinterpret_cast<uint32_t*>(cur_launch + (uint64_t)P->P * kTicketStride * 4 + kStatsWords * 8 + 128);
   a.zero_launch = reinterpret_cast<uint32_t*>(P->ws + L.launch[lb ^ 1u]);
@@ -467,25 +501,26 @@ static int launch_engine(tc_plan* P) {
   return TC_OK;
 }
 
-// Runs the check kernel on the engine stream and reads the flags back.
-static int run_check(tc_plan* P) {
+// Queues the check kernel on the engine stream behind the engine and behind
+// the producer's work queued so far; it writes its per-chunk flags and the
+// engine status straight into mapped pinned memory.
+static int queue_check(tc_plan* P) {
+  TC_HIP(hipEventRecord(P->ev_prod_end, P->producer_stream));
+  TC_HIP(hipStreamWaitEvent(P->engine_stream, P->ev_prod_end, 0));
   CheckArgs c{};
   c.chunks = reinterpret_cast<const ChunkD*>(P->ws + P->L.chunks);
   c.gates = P->ws + P->L.gates;
   c.gate_stride = P->L.gate_stride;
-  c.flags = reinterpret_cast<uint32_t*>(P->ws + P->L.check);
+  c.flags = P->flags_dev;
+  c.status = reinterpret_cast<uint32_t*>(P->ws + P->L.status);
+  c.status_host = P->status_dev;
   c.G = P->G;
   c.nranks = P->P;
   c.round = P->round;
-  if (P->G > 0) {
-    hipLaunchKernelGGL(check_kernel, dim3((P->G + 255) / 256), dim3(256), 0, P->engine_stream, c);
-    TC_HIP(hipGetLastError());
-    TC_HIP(hipMemcpyAsync(P->flags_host, c.flags, (size_t)P->G * 4, hipMemcpyDeviceToHost,
-                          P->engine_stream));
-  }
-  TC_HIP(hipMemcpyAsync(P->status_host, P->ws + P->L.status, 4, hipMemcpyDeviceToHost,
-                        P->engine_stream));
-  TC_HIP(hipStreamSynchronize(P->engine_stream));
+  const uint32_t blocks = std::max<uint32_t>(1, (P->G + 255) / 256);
+  hipLaunchKernelGGL(check_kernel, dim3(blocks), dim3(256), 0, P->engine_stream, c);
+  TC_HIP(hipGetLastError());
+  TC_HIP(hipEventRecord(P->ev_check_done, P->engine_stream));
   return TC_OK;
 }
 
@@ -543,9 +578,9 @@ int tc_plan_validate(const tc_plan_desc* d) {
 
 static void destroy(tc_plan* P) {
   if (!P) return;
-  if (P->engine_stream) (void)hipStreamDestroy(P->engine_stream);
   if (P->aux_stream) (void)hipStreamDestroy(P->aux_stream);
-  for (hipEvent_t e : {P->ev_prod_start, P->ev_prod_end, P->ev_engine_start, P->ev_engine_done})
+  for (hipEvent_t e : {P->ev_prod_start, P->ev_prod_end, P->ev_engine_start, P->ev_engine_done,
+                       P->ev_check_done})
     if (e) (void)hipEventDestroy(e);
   if (P->abort_host) (void)hipHostFree((void*)P->abort_host);
   if (P->flags_host) (void)hipHostFree(P->flags_host);
@@ -608,19 +643,23 @@ int tc_plan_create(const tc_plan_desc* d, tc_plan** out) {
   uint32_t usable = 0;
   for (uint32_t m : mask) usable += __builtin_popcount(m);
   if (usable == 0) return bail(fail(TC_EINVAL, "cu_mask selects no CU"));
-  TC_HIP_C(hipExtStreamCreateWithCUMask(&P->engine_stream, (uint32_t)mask.size(), mask.data()));
+  if ((rc = engine_stream_for(P->device, mask, &P->engine_stream))) return bail(rc);
   TC_HIP_C(hipStreamCreateWithFlags(&P->aux_stream, hipStreamNonBlocking));
   TC_HIP_C(hipEventCreateWithFlags(&P->ev_prod_start, hipEventDisableTiming));
   TC_HIP_C(hipEventCreateWithFlags(&P->ev_prod_end, hipEventDisableTiming));
   TC_HIP_C(hipEventCreate(&P->ev_engine_start));
   TC_HIP_C(hipEventCreate(&P->ev_engine_done));
+  TC_HIP_C(hipEventCreateWithFlags(&P->ev_check_done, hipEventDisableTiming));
   void* hp = nullptr;
   TC_HIP_C(hipHostMalloc(&hp, 64, hipHostMallocMapped | hipHostMallocCoherent));
   P->abort_host = (volatile uint32_t*)hp;
   P->abort_host[0] = 0;
   TC_HIP_C(hipHostGetDevicePointer((void**)&P->abort_dev, hp, 0));
-  TC_HIP_C(hipHostMalloc((void**)&P->flags_host, (size_t)std::max<uint32_t>(P->G, 1) * 4, 0));
-  TC_HIP_C(hipHostMalloc((void**)&P->status_host, 64, 0));
+  TC_HIP_C(hipHostMalloc((void**)&P->flags_host, (size_t)std::max<uint32_t>(P->G, 1) * 4,
+                         hipHostMallocMapped | hipHostMallocCoherent));
+  TC_HIP_C(hipHostGetDevicePointer((void**)&P->flags_dev, P->flags_host, 0));
+  TC_HIP_C(hipHostMalloc((void**)&P->status_host, 64, hipHostMallocMapped | hipHostMallocCoherent));
+  TC_HIP_C(hipHostGetDevicePointer((void**)&P->status_dev, P->status_host, 0));
 
   // Zero the workspace (gates start at zero, [TP] Gates and rounds), then
   // upload the descriptors once.
@@ -643,10 +682,21 @@ int tc_plan_create(const tc_plan_desc* d, tc_plan** out) {
   }
   TC_HIP_C(hipMemcpy(P->ws + P->L.wprefix, wprefix.data(), wprefix.size() * 8, hipMemcpyHostToDevice));
 
-  // Default: 4 CTAs of 4 waves per usable CU (16 worker waves per CU), but
-  // no more waves than pieces.
+  // Default engine size: one worker wave per piece up to 256 (small rounds
+  // are latency-bound: every piece in flight at once), otherwise one wave per
+  // 64 KiB of source bytes per round, at most 16 per usable CU (the count
+  // that saturates HBM).  Fewer waves leave the producer's CUs quieter when a
+  // round moves little data.
   const uint32_t npieces = (uint32_t)P->pieces.size();
-  P->engine_ctas = d->engine_ctas ? d->engine_ctas : 4 * usable;
+  uint64_t src_bytes = 0;
+  for (const ChunkD& c : P->chunks) src_bytes += c.bytes;
+  if (d->engine_ctas) {
+    P->engine_ctas = d->engine_ctas;
+  } else {
+    const uint64_t waves = std::min<uint64_t>(
+        16ull * usable, std::max<uint64_t>(std::min<uint64_t>(npieces, 256), src_bytes >> 16));
+    P->engine_ctas = (uint32_t)((waves + 3) / 4);
+  }
   P->engine_ctas = std::max<uint32_t>(1, std::min<uint32_t>(P->engine_ctas, (std::max<uint32_t>(npieces, 1) + 3) / 4));
   const uint64_t backstop_us = d->engine_backstop_us ? d->engine_backstop_us : 30ull * 1000 * 1000;
   P->backstop_ticks = backstop_us * 100;  // s_memrealtime runs at 100 MHz
@@ -690,31 +740,34 @@ int tc_plan_wait(tc_plan* P, uint64_t timeout_us) {
     if (int rc = launch_engine(P)) return rc;
     P->need_relaunch = false;
   }
-  TC_HIP(hipEventRecord(P->ev_prod_end, P->producer_stream));
+  // One event covers everything: the check runs after the engine and after
+  // the producer's work, so extra marks issued after the gate opened count.
+  if (int rc = queue_check(P)) return rc;
   const auto deadline = std::chrono::steady_clock::now() + std::chrono::microseconds(timeout_us);
   hipError_t err = hipSuccess;
-  int e1 = event_done_by(P->ev_engine_done, deadline, &err);
-  int e2 = e1 == 1 ? event_done_by(P->ev_prod_end, deadline, &err) : 0;
-  if (e1 < 0 || e2 < 0) return hip_fail(err, "hipEventQuery");
-  bool timed_out = !(e1 == 1 && e2 == 1);
-  if (timed_out && e1 != 1) {
-    // Stop this launch of the engine; every poll loop watches the word.
-    __atomic_store_n(P->abort_host, P->launch_id, __ATOMIC_SEQ_CST);
+  const int done = event_done_by(P->ev_check_done, deadline, &err);
+  if (done < 0) return hip_fail(err, "hipEventQuery");
+  const bool timed_out = done == 0;
+  if (timed_out) {
+    // Stop this launch of the engine if it still runs (every poll loop
+    // watches the abort word), then let the queued check finish.
+    if (hipEventQuery(P->ev_engine_done) != hipSuccess)
+      __atomic_store_n(P->abort_host, P->launch_id, __ATOMIC_SEQ_CST);
     const auto drain = std::chrono::steady_clock::now() + std::chrono::seconds(10);
-    int e3 = event_done_by(P->ev_engine_done, drain, &err);
+    const int e3 = event_done_by(P->ev_check_done, drain, &err);
     if (e3 < 0) return hip_fail(err, "hipEventQuery");
-    if (e3 == 0)
-      return fail(TC_ETIMEOUT, "wait: copy engine did not stop within 10 s of the abort");
+    if (e3 == 0) {
+      P->need_relaunch = hipEventQuery(P->ev_engine_done) == hipSuccess;
+      return fail(TC_ETIMEOUT, "wait: the copy engine or the producer did not finish within 10 s "
+                               "of the deadline");
+    }
   }
   TC_HIP(hipEventElapsedTime(&P->last_engine_ms, P->ev_engine_start, P->ev_engine_done));
-  if (int rc = run_check(P)) return rc;
-  const uint32_t st = P->status_host[0];
+  const uint32_t st = __atomic_load_n(P->status_host, __ATOMIC_ACQUIRE);
   if (st & (kStatusAborted | kStatusExpired)) P->need_relaunch = true;
-  // Clear the status word for the next launch (a fill kernel, not a memset).
-  if (int rc = zero_device(P->ws + P->L.status, 4, P->engine_stream)) return rc;
   bool extra = false, corrupt = false, shortc = false;
   for (uint32_t g = 0; g < P->G; ++g) {
-    const uint32_t f = P->flags_host[g];
+    const uint32_t f = __atomic_load_n(P->flags_host + g, __ATOMIC_ACQUIRE);
     if (f & kFlagExtra) extra = true;
     if (f & kFlagCorrupt) corrupt = true;
     if (f & (kFlagShortMarks | kFlagNotOpen | kFlagNotArrived)) shortc = true;
@@ -830,13 +883,13 @@ int tc_plan_stats(tc_plan* P, tc_stats* out) {
   out->pieces = P->pieces.size();
   out->G = P->G;
   if (P->launch_seq) {
-    uint64_t st[kStatsWords] = {0};
+    uint32_t st[2] = {0, 0};
     const uint8_t* blk = P->ws + P->L.launch[P->cur_launch_block];
     TC_HIP(hipMemcpyAsync(st, blk + (uint64_t)P->P * kTicketStride * 4, sizeof(st),
                           hipMemcpyDeviceToHost, P->aux_stream));
     TC_HIP(hipStreamSynchronize(P->aux_stream));
-    const uint64_t first = ~st[0];
-    if (st[0] && st[1] >= first) out->window_ticks = st[1] - first;
+    const uint32_t first = ~st[0];
+    if (st[0] && st[1]) out->window_ticks = (uint32_t)(st[1] - first);  // modulo 2^32
   }
   return TC_OK;
 }

@@ -58,10 +58,13 @@ struct tc_plan {
   hipStream_t producer_stream = nullptr;
   hipEvent_t ev_prod_start = nullptr, ev_prod_end = nullptr;
   hipEvent_t ev_engine_start = nullptr, ev_engine_done = nullptr;
+  hipEvent_t ev_check_done = nullptr;
   volatile uint32_t* abort_host = nullptr;  // pinned, mapped
   uint32_t* abort_dev = nullptr;
-  uint32_t* flags_host = nullptr;           // pinned
-  uint32_t* status_host = nullptr;          // pinned
+  uint32_t* flags_host = nullptr;           // pinned, mapped: check-kernel output
+  uint32_t* flags_dev = nullptr;
+  uint32_t* status_host = nullptr;          // pinned, mapped: engine status of the last launch
+  uint32_t* status_dev = nullptr;
 
   uint32_t engine_ctas = 0;
   uint64_t backstop_ticks = 0;
