@@ -329,7 +329,8 @@ typedef struct tc_fill_desc {
 int tc_produce_fill(tc_plan* plan, const tc_handle* h, const tc_fill_desc* d, void* stream);
 
 /* Deferred marks: every chunk of every rank receives exactly its writers'
- * marks, one CTA per mark, on `stream`. */
+ * marks, one CTA per mark, on `stream`.  The plan may be READY or STARTED
+ * (marks that precede start() simply find the engine's gates open). */
 int tc_mark_all(tc_plan* plan, const tc_handle* h, void* stream);
 
 /* `count` marks of rank `rank`'s chunk `chunk`, one CTA each, on `stream`

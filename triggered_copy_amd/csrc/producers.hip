@@ -274,6 +274,8 @@ int tc_produce_fill(tc_plan* P, const tc_handle* h, const tc_fill_desc* d, void*
 
 int tc_mark_all(tc_plan* P, const tc_handle* h, void* stream) {
   if (!P || !h) return fail(TC_EINVAL, "mark_all: NULL argument");
+  if ((P->state != TC_STATE_READY && P->state != TC_STATE_STARTED) || h->round != P->round)
+    return fail(TC_ESTATE, "mark_all: the handle is not this plan's current round");
   if (P->total_writers == 0) return TC_OK;
   if (P->total_writers > 0x7FFFFFFFull) return fail(TC_EINVAL, "mark_all: too many writers");
   MarkArgs a{};
