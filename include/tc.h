@@ -105,10 +105,18 @@ typedef struct tc_chunk {
 } tc_chunk;
 
 /* A 64-byte gate row ([TP] Gates and rounds: ready, arrival and a writer
- * counter; the copy side polls the low 32 bits of ready with >=).  In rank
- * p's own table the row of its chunk c holds ready (= the last opened round)
- * and writers (cumulative marks); in a peer q's table the same row holds
- * arrival (= rounds delivered to q).  Bytes 24..63 stay zero. */
+ * counter; the copy side polls the gate against the round with >=).  As
+ * reported by tc_plan_read_gates: in rank p's own table the row of its chunk
+ * c holds ready (= the last round whose gate opened) and writers (cumulative
+ * marks); in a peer q's table the same row holds arrival (= rounds delivered
+ * to q).  Bytes 24..63 are zero.
+ *
+ * On the device only `arrival` is stored in the rows.  The writer count is
+ * kept in TC_MARK_STRIPES counters per chunk, TC_MARK_STRIPE_BYTES apart, so
+ * that the marks of many CTAs finishing together do not queue on one
+ * address; a mark adds 1 to one of them.  The count is their sum, the gate
+ * of round r is open when the count reaches r * writers, and `ready` is the
+ * derived value min(count / writers, round). */
 typedef struct tc_gate_row {
   uint64_t ready;
   uint64_t arrival;
@@ -116,13 +124,19 @@ typedef struct tc_gate_row {
   uint64_t rsvd[5];
 } tc_gate_row;
 
+#define TC_MARK_STRIPES 8
+#define TC_MARK_STRIPE_BYTES 128
+
 /* What start() hands to kernels, by value ([TP] Model: handle = plan.start(),
- * passed to the producer).  Gate row of rank src's chunk c in rank q's table:
- *   gates + q*gate_stride + (chunk_base[src] + c) * 64. */
+ * passed to the producer).  Arrival row of rank src's chunk c in rank q's
+ * table: gates + q*gate_stride + (chunk_base[src] + c) * 64.  Mark stripe s
+ * of global chunk g: the uint64 at marks + (g*TC_MARK_STRIPES + s) *
+ * TC_MARK_STRIPE_BYTES. */
 typedef struct tc_handle {
   uint64_t gates;        /* device address of rank 0's gate table */
   uint64_t gate_stride;  /* bytes between consecutive ranks' gate tables */
   uint64_t writers;      /* device address of uint32 writers[G], by global chunk id */
+  uint64_t marks;        /* device address of the mark stripes */
   uint32_t round;        /* this round, >= 1 */
   uint32_t nranks;       /* P */
   uint32_t chunk_base[TC_MAX_RANKS + 1]; /* [P] = total chunks G */
@@ -266,7 +280,9 @@ int tc_plan_state(const tc_plan* plan, int* state, uint32_t* round);
  * rank_chunk[2i], rank_chunk[2i+1]; *n = the total number. */
 int tc_plan_problems(const tc_plan* plan, uint32_t* rank_chunk, uint32_t cap, uint32_t* n);
 
-/* Synchronous snapshot of all gate tables: P x G x 64 bytes into host. */
+/* Synchronous snapshot of all gate tables: P x G x 64 bytes into host, rows
+ * as tc_gate_row describes (ready and writers derived from the mark stripes
+ * against the plan's current round). */
 int tc_plan_read_gates(tc_plan* plan, void* host, uint64_t bytes);
 
 /* Synchronous snapshot of the queue cursors: host[p*P + q] = chunks of rank
@@ -344,8 +360,8 @@ int tc_mark(tc_plan* plan, const tc_handle* h, uint32_t rank, uint32_t chunk,
  * 128x128 tiles; program p takes steps p, p + programs, ...; step s computes
  * tile tc_tile_of(s, tm, tn, group_m) and, when h != NULL, then marks chunk
  * first_chunk + s / tiles_per_chunk of rank `rank`.  A, Bt, C device.
- * C is stored with system-scope write-through stores, so the release in
- * mark_ready has little left to write back.
+ * C is stored with system-scope write-through stores, so its marks need no
+ * L2 write-back (tc_mark_ready_wt).
  * TC_EINVAL unless K % 8 == 0, N % 8 == 0, ldc % 8 == 0, ldc < 2^23, pointers
  * 16-byte aligned. */
 int tc_gemm_bf16(const void* A, const void* Bt, void* C, uint32_t M, uint32_t N, uint32_t K,

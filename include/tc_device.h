@@ -4,10 +4,12 @@
  * Producer side ([TP] = "Triggered Plans", section Memory ordering): a chunk's
  * data must be in memory before its gate opens.  Every wave waits for its own
  * stores (s_waitcnt vmcnt(0)), the CTA barrier makes that true for every wave,
- * then one thread adds 1 to the chunk's writer counter with a release at
- * system scope (which writes back this XCD's L2); the writer whose increment
- * completes the round's count then stores the round into `ready`.  The gate
- * store itself needs no release: it follows the releasing increment.
+ * then one thread releases (writing back this XCD's L2) and adds 1 to the
+ * chunk's writer count.  The count is striped over TC_MARK_STRIPES words so
+ * that hundreds of writer CTAs finishing together do not serialize on one
+ * address; the gate of round r is open once the stripes sum to r * writers.
+ * Nobody needs to learn that it was the last writer, so the increment does
+ * not wait for its result.
  *
  * Consumer side (same section; [TP] The kernel author's contract, item 5):
  * arrived/wait read the arrival counter, then acquire at system scope.  One
@@ -17,10 +19,10 @@
  * every thread of the CTA must make them, outside divergent branches.
  *
  * Gate rows: rank src's chunk c has global id chunk_base[src] + c; its row in
- * rank q's table is at gates + q * gate_stride + id * 64.  `ready` and the
- * writer counter live in the sender's own table (q == src), `arrival` in
- * each receiver's table.  A rank's own chunk never "arrives" at itself:
- * tc_arrived(dst == src) means its gate is open.
+ * rank q's table is at gates + q * gate_stride + id * 64, and holds the
+ * chunk's `arrival` at q.  The mark stripes of global chunk g start at
+ * marks + g * TC_MARK_STRIPES * TC_MARK_STRIPE_BYTES.  A rank's own chunk
+ * never "arrives" at itself: tc_arrived(dst == src) means its gate is open.
  */
 #ifndef TC_DEVICE_H
 #define TC_DEVICE_H
@@ -71,35 +73,69 @@ __device__ inline uint64_t tc_uniform64(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-/* mark_ready(chunk) by one writer CTA of rank `rank`.  Whole CTA.  The
- * leader thread alone does the increment: a 64-bit release atomic issued by a
- * whole wave would be 64 serialized atomics.  The leader block holds no loop
- * and is followed by the closing barrier, so it cannot be merged into a
- * caller's loop back-edge. */
-__device__ inline void tc_mark_ready(const tc_handle& h, uint32_t rank, uint32_t chunk) {
+/* Mark stripe s of rank src's chunk c. */
+__device__ inline uint64_t* tc_mark_stripe(const tc_handle& h, uint32_t src, uint32_t chunk,
+                                           uint32_t s) {
+  return reinterpret_cast<uint64_t*>(
+      h.marks + ((uint64_t)(h.chunk_base[src] + chunk) * TC_MARK_STRIPES + s) * TC_MARK_STRIPE_BYTES);
+}
+
+/* mark_ready(chunk) by one writer CTA of rank `rank`.  Whole CTA.  Every
+ * wave waits for its stores, the barrier makes that true for the CTA, then
+ * the leader thread releases at agent scope (the L2 write-back that makes
+ * the chunk's bytes visible to every XCD) and adds 1 to one of the chunk's
+ * mark stripes, chosen by the CTA index, without waiting for the result.
+ * Whoever polls the gate sums the stripes.  kWriteBack = false skips the
+ * write-back: only for producers whose every store to the chunk was issued
+ * write-through at system scope, so that its completion (vmcnt) already
+ * made the bytes visible.  The leader block holds no loop and is followed by
+ * the closing barrier, so it cannot be merged into a caller's loop back-edge. */
+template <bool kWriteBack>
+__device__ inline void tc_mark_ready_impl(const tc_handle& h, uint32_t rank, uint32_t chunk) {
   __builtin_amdgcn_s_waitcnt(TC_WAITCNT_VMCNT0);  // this wave's stores are done
   __syncthreads();                                // ... and so are every other wave's
   if (tc_is_cta_leader()) {
-    tc_gate_row* row = tc_gate_row_ptr(h, rank, rank, chunk);
-    const uint32_t* writers = reinterpret_cast<const uint32_t*>(h.writers);
-    const uint64_t w = writers[h.chunk_base[rank] + chunk];
-    const uint64_t old = __hip_atomic_fetch_add(&row->writers, (uint64_t)1, __ATOMIC_RELEASE,
-                                                __HIP_MEMORY_SCOPE_SYSTEM);
-    if (old + 1 == (uint64_t)h.round * w)          // the last writer of this round
-      __hip_atomic_store(&row->ready, (uint64_t)h.round, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_SYSTEM);
+    uint64_t* stripe = tc_mark_stripe(h, rank, chunk, blockIdx.x % TC_MARK_STRIPES);
+    if (kWriteBack) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_fetch_add(stripe, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
 }
 
+__device__ inline void tc_mark_ready(const tc_handle& h, uint32_t rank, uint32_t chunk) {
+  tc_mark_ready_impl<true>(h, rank, chunk);
+}
+
+/* mark_ready for producers that store the chunk with system-scope
+ * write-through stores (cache policy sc0 sc1) only. */
+__device__ inline void tc_mark_ready_wt(const tc_handle& h, uint32_t rank, uint32_t chunk) {
+  tc_mark_ready_impl<false>(h, rank, chunk);
+}
+
+/* The chunk's mark count: the sum of its stripes (relaxed, wave-uniform). */
+__device__ inline uint64_t tc_mark_count(const tc_handle& h, uint32_t src, uint32_t chunk) {
+  uint64_t sum = 0;
+#pragma unroll
+  for (uint32_t s = 0; s < TC_MARK_STRIPES; ++s)
+    sum += tc_uniform64(__hip_atomic_load(tc_mark_stripe(h, src, chunk, s), __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT));
+  return sum;
+}
+
 /* One relaxed poll of chunk (src, chunk) as seen by rank dst, wave-uniform:
- * every lane reads the same word.  The caller acquires after a true result. */
+ * every lane reads the same words.  dst == src: the gate is open (the mark
+ * count reached round * writers); otherwise the chunk's arrival at dst
+ * reached the round.  The caller acquires after a true result. */
 __device__ inline bool tc_poll_once(const tc_handle& h, uint32_t dst, uint32_t src,
                                     uint32_t chunk) {
-  tc_gate_row* row = tc_gate_row_ptr(h, dst, src, chunk);
-  const uint64_t* field = (dst == src) ? &row->ready : &row->arrival;
+  if (dst == src) {
+    const uint32_t* writers = reinterpret_cast<const uint32_t*>(h.writers);
+    const uint64_t w = writers[h.chunk_base[src] + chunk];
+    return tc_mark_count(h, src, chunk) >= (uint64_t)h.round * w;
+  }
+  const tc_gate_row* row = tc_gate_row_ptr(h, dst, src, chunk);
   const uint32_t lo = tc_uniform(
-      (uint32_t)__hip_atomic_load(field, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM));
+      (uint32_t)__hip_atomic_load(&row->arrival, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM));
   return lo >= h.round;
 }
 

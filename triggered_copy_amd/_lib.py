@@ -33,7 +33,7 @@ class Chunk(C.Structure):
 
 
 class Handle(C.Structure):
-    _fields_ = [("gates", u64), ("gate_stride", u64), ("writers", u64), ("round", u32),
+    _fields_ = [("gates", u64), ("gate_stride", u64), ("writers", u64), ("marks", u64), ("round", u32),
                 ("nranks", u32), ("chunk_base", u32 * (TC_MAX_RANKS + 1)), ("rsvd", u32)]
 
 

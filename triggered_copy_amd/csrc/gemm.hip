@@ -145,9 +145,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
         }
     __syncthreads();
     // 128 rows x 16 vectors of 8 bf16: 8 vectors per thread, stored through
-    // to memory at system scope, so that the release in mark_ready finds
-    // nothing of this tile left to write back.  Lanes outside the matrix get
-    // an offset past the buffer range and their stores are dropped.
+    // to memory at system scope, so that once they complete the tile is
+    // visible everywhere and mark_ready needs no L2 write-back.  Lanes
+    // outside the matrix get an offset past the buffer range and their
+    // stores are dropped.
     const uint32_t rows_in = a.M - m0 < (uint32_t)BM ? a.M - m0 : (uint32_t)BM;
     const uint32_t cols_in = a.N - n0 < (uint32_t)BN ? a.N - n0 : (uint32_t)BN;
     const uint32_t extent = (uint32_t)(((uint64_t)(rows_in - 1) * a.ldc + cols_in) * 2);
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
       __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(lds + r * LDC + c), rc,
                                              (int)off, 0, 17 /* sc0 sc1 */);
     }
-    if (a.mark) tc_mark_ready(a.h, a.rank, a.first_chunk + step / a.tiles_per_chunk);
+    if (a.mark) tc_mark_ready_wt(a.h, a.rank, a.first_chunk + step / a.tiles_per_chunk);
   }
 }
 

@@ -70,6 +70,7 @@ Layout compute_layout(uint32_t P, uint32_t G, uint64_t npieces) {
   L.pieces = take(npieces * sizeof(PieceD));
   L.chunks = take((uint64_t)G * sizeof(ChunkD));
   L.writers = take((uint64_t)G * 4);
+  L.marks = take((uint64_t)G * TC_MARK_STRIPES * TC_MARK_STRIPE_BYTES);
   L.wprefix = take((uint64_t)(G + 1) * 8);
   // tickets (one line per source) | stats | stop word | done (one line per chunk)
   L.launch_bytes = align_up((uint64_t)P * kTicketStride * 4 + kStatsWords * 8 + 128 +
@@ -80,7 +81,6 @@ Layout compute_layout(uint32_t P, uint32_t G, uint64_t npieces) {
   L.round_blk[0] = take(L.round_bytes);
   L.round_blk[1] = take(L.round_bytes);
   L.status = take(256);
-  L.check = take((uint64_t)std::max<uint32_t>(G, 1) * 4);
   L.total = off;
   return L;
 }
@@ -115,6 +115,7 @@ struct EngineArgs {
   const ChunkD* chunks;
   uint8_t* gates;
   uint64_t gate_stride;
+  const uint8_t* marks;   // mark stripes, TC_MARK_STRIPES per chunk
   uint32_t* tickets;      // this launch: one per source, kTicketStride apart
   uint32_t* done;         // this launch: pieces finished, per chunk, kTicketStride apart
   uint32_t* stats;        // this launch: [0] ~first gate seen, [1] last signal (low 32 bits
@@ -182,17 +183,15 @@ __device__ inline bool must_stop(const EngineArgs& a, uint64_t t0, uint32_t spin
   return true;
 }
 
-// Uniform spin until the u32 at `word` is >= target.  Waves sleep longer
-// the longer they wait; "reserve" waves (all but one in eight) sleep about
-// 20 us between polls once they have waited a little, so thousands of idle
-// workers put almost no load on the memory system while a producer runs.
-__device__ inline bool poll_ge(const EngineArgs& a, const uint32_t* word, uint32_t target,
-                               uint64_t t0, bool reserve, uint32_t* seen) {
+// Uniform spin until ready() holds.  Waves sleep longer the longer they
+// wait; "reserve" waves (all but one in eight) sleep about 20 us between
+// polls once they have waited a little, so thousands of idle workers put
+// almost no load on the memory system while a producer runs.
+template <typename Ready>
+__device__ inline bool poll_until(const EngineArgs& a, uint64_t t0, bool reserve, Ready ready) {
   uint32_t spins = 0;
   for (;;) {
-    const uint32_t v = wave_load_sys(word);
-    if (v >= target) {
-      if (seen) *seen = v;
+    if (ready()) {
       asm volatile("" ::: "memory");  // no later access is moved above the poll
       return true;
     }
@@ -208,6 +207,18 @@ __device__ inline bool poll_ge(const EngineArgs& a, const uint32_t* word, uint32
   }
 }
 
+// The mark count of global chunk g: the sum of its stripes.  Uniform.
+__device__ inline uint64_t mark_count(const EngineArgs& a, uint32_t g) {
+  const uint64_t* s = reinterpret_cast<const uint64_t*>(a.marks + (uint64_t)g * TC_MARK_STRIPES *
+                                                                       TC_MARK_STRIPE_BYTES);
+  uint64_t sum = 0;
+#pragma unroll
+  for (uint32_t k = 0; k < TC_MARK_STRIPES; ++k)
+    sum += tc_uniform64(__hip_atomic_load(s + k * (TC_MARK_STRIPE_BYTES / 8), __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT));
+  return sum;
+}
+
 __device__ inline tc_gate_row* gate_row(const EngineArgs& a, uint32_t table, uint32_t g) {
   return reinterpret_cast<tc_gate_row*>(a.gates + (uint64_t)table * a.gate_stride +
                                         (uint64_t)g * TC_GATE_ROW_BYTES);
@@ -220,7 +231,7 @@ __device__ bool signal_in_order(const EngineArgs& a, uint32_t p, uint32_t c, uin
                                 uint64_t t0) {
   uint32_t* sig = a.sig + p * kTicketStride;
   uint32_t seen = 0;
-  if (!poll_ge(a, sig, c, t0, false, &seen)) return false;
+  if (!poll_until(a, t0, false, [&] { return (seen = wave_load_sys(sig)) >= c; })) return false;
   if (seen > c) return true;  // signalled by an earlier launch of this round
   const uint64_t one = tc_lane_id() == 0 ? 1u : 0u;
   for (uint32_t q = 0; q < a.nranks; ++q) {
@@ -348,8 +359,9 @@ __global__ __launch_bounds__(kEngineThreads) void engine_kernel(EngineArgs a) {
       const PieceD pc = a.pieces[a.piece_base[p] + t];
       const uint32_t g = tc_uniform(pc.chunk);
       if (g != acquired) {
-        const uint32_t* ready = reinterpret_cast<const uint32_t*>(&gate_row(a, p, g)->ready);
-        if (!poll_ge(a, ready, a.round, t0, reserve, nullptr)) return;
+        // The gate of round r is open once the chunk's marks reach r * writers.
+        const uint64_t want = (uint64_t)a.round * tc_uniform(a.chunks[g].writers);
+        if (!poll_until(a, t0, reserve, [&] { return mark_count(a, g) >= want; })) return;
         // The wave holding a chunk's first piece records when it saw the gate open.
         if (a.piece_base[p] + t == a.chunks[g].first_piece) wave_max32(&a.stats[0], ~(uint32_t)now_ticks());
         acquired = g;
@@ -370,6 +382,7 @@ struct CheckArgs {
   const ChunkD* chunks;
   const uint8_t* gates;
   uint64_t gate_stride;
+  const uint8_t* marks;
   uint32_t* flags;        // mapped pinned host memory, one word per chunk
   uint32_t* status;       // device engine status word: read, reported, cleared
   uint32_t* status_host;  // mapped pinned host memory
@@ -380,9 +393,9 @@ __device__ inline uint64_t ld(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// One thread per global chunk: compare its gate rows with what a complete
-// round r leaves ([TP] Gates and rounds: this rank's chunk marked ready and
-// arrived at every peer).
+// One thread per global chunk: compare its counters with what a complete
+// round r leaves ([TP] Gates and rounds: this rank's chunk marked by all its
+// writers and arrived at every peer).
 __global__ void check_kernel(CheckArgs a) {
   const uint32_t g = blockIdx.x * blockDim.x + threadIdx.x;
   if (g == 0) {  // hand the engine's status to the host and clear it for the next launch
@@ -397,22 +410,25 @@ __global__ void check_kernel(CheckArgs a) {
     return reinterpret_cast<const tc_gate_row*>(a.gates + (uint64_t)q * a.gate_stride +
                                                 (uint64_t)g * TC_GATE_ROW_BYTES);
   };
+  uint64_t marks = 0;
+  for (uint32_t k = 0; k < TC_MARK_STRIPES; ++k)
+    marks += ld(reinterpret_cast<const uint64_t*>(
+        a.marks + ((uint64_t)g * TC_MARK_STRIPES + k) * TC_MARK_STRIPE_BYTES));
   uint32_t f = 0;
-  const tc_gate_row* own = row(cd.rank);
-  const uint64_t w = ld(&own->writers);
-  if (w > want) f |= kFlagExtra;
-  if (w < want) f |= kFlagShortMarks;
-  if ((uint32_t)ld(&own->ready) < a.round) f |= kFlagNotOpen;
-  if (ld(&own->arrival) != 0) f |= kFlagCorrupt;
+  if (marks > want) f |= kFlagExtra;
+  if (marks < want) f |= kFlagShortMarks;
   for (uint32_t q = 0; q < a.nranks; ++q) {
     const tc_gate_row* r = row(q);
     for (int k = 0; k < 5; ++k)
       if (ld(&r->rsvd[k]) != 0) f |= kFlagCorrupt;
-    if (q == cd.rank) continue;
+    if (ld(&r->ready) != 0 || ld(&r->writers) != 0) f |= kFlagCorrupt;
     const uint64_t arr = ld(&r->arrival);
+    if (q == cd.rank) {
+      if (arr != 0) f |= kFlagCorrupt;
+      continue;
+    }
     if (arr < a.round) f |= kFlagNotArrived;
     if (arr > a.round) f |= kFlagCorrupt;
-    if (ld(&r->ready) != 0 || ld(&r->writers) != 0) f |= kFlagCorrupt;
   }
   __hip_atomic_store(a.flags + g, f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
@@ -470,6 +486,7 @@ static int launch_engine(tc_plan* P) {
   a.chunks = reinterpret_cast<const ChunkD*>(P->ws + L.chunks);
   a.gates = P->ws + L.gates;
   a.gate_stride = L.gate_stride;
+  a.marks = P->ws + L.marks;
   const uint32_t lb = P->launch_seq & 1u;  // launch block of this launch
   uint8_t* cur_launch = P->ws + L.launch[lb];
   a.tickets = reinterpret_cast<uint32_t*>(cur_launch);
@@ -511,6 +528,7 @@ static int queue_check(tc_plan* P) {
   c.chunks = reinterpret_cast<const ChunkD*>(P->ws + P->L.chunks);
   c.gates = P->ws + P->L.gates;
   c.gate_stride = P->L.gate_stride;
+  c.marks = P->ws + P->L.marks;
   c.flags = P->flags_dev;
   c.status = reinterpret_cast<uint32_t*>(P->ws + P->L.status);
   c.status_host = P->status_dev;
@@ -770,7 +788,7 @@ int tc_plan_wait(tc_plan* P, uint64_t timeout_us) {
     const uint32_t f = __atomic_load_n(P->flags_host + g, __ATOMIC_ACQUIRE);
     if (f & kFlagExtra) extra = true;
     if (f & kFlagCorrupt) corrupt = true;
-    if (f & (kFlagShortMarks | kFlagNotOpen | kFlagNotArrived)) shortc = true;
+    if (f & (kFlagShortMarks | kFlagNotArrived)) shortc = true;
   }
   auto collect = [&](uint32_t mask) {
     for (uint32_t g = 0; g < P->G; ++g)
@@ -790,7 +808,7 @@ int tc_plan_wait(tc_plan* P, uint64_t timeout_us) {
     return fail(TC_ECORRUPT, "wait: gate rows hold values no correct round produces");
   }
   if (shortc || timed_out || P->need_relaunch) {
-    collect(kFlagShortMarks | kFlagNotOpen | kFlagNotArrived);
+    collect(kFlagShortMarks | kFlagNotArrived);
     if (!P->need_relaunch && shortc) P->need_relaunch = true;
     return fail(TC_ETIMEOUT, "wait: timed out with " + std::to_string(P->problems.size() / 2) +
                                  " chunk(s) still short");
@@ -855,11 +873,27 @@ int tc_plan_read_gates(tc_plan* P, void* host, uint64_t bytes) {
   if (!P || !host) return fail(TC_EINVAL, "read_gates: NULL argument");
   const uint64_t need = (uint64_t)P->P * P->G * TC_GATE_ROW_BYTES;
   if (bytes < need) return fail(TC_EINVAL, "read_gates: need " + std::to_string(need) + " bytes");
-  for (uint32_t q = 0; q < P->P && P->G; ++q)
+  if (P->G == 0) return TC_OK;
+  std::vector<uint64_t> marks((size_t)P->G * TC_MARK_STRIPES * (TC_MARK_STRIPE_BYTES / 8));
+  for (uint32_t q = 0; q < P->P; ++q)
     TC_HIP(hipMemcpyAsync((uint8_t*)host + (uint64_t)q * P->G * TC_GATE_ROW_BYTES,
                           P->ws + P->L.gates + q * P->L.gate_stride,
                           (size_t)P->G * TC_GATE_ROW_BYTES, hipMemcpyDeviceToHost, P->aux_stream));
+  TC_HIP(hipMemcpyAsync(marks.data(), P->ws + P->L.marks, marks.size() * 8, hipMemcpyDeviceToHost,
+                        P->aux_stream));
   TC_HIP(hipStreamSynchronize(P->aux_stream));
+  // The sender's row: writers = the stripes' sum, ready = the last round
+  // whose gate that count opened (at most the current round).
+  for (uint32_t g = 0; g < P->G; ++g) {
+    const ChunkD& cd = P->chunks[g];
+    uint64_t count = 0;
+    for (uint32_t k = 0; k < TC_MARK_STRIPES; ++k)
+      count += marks[((size_t)g * TC_MARK_STRIPES + k) * (TC_MARK_STRIPE_BYTES / 8)];
+    auto* row = reinterpret_cast<tc_gate_row*>((uint8_t*)host +
+                                               ((uint64_t)cd.rank * P->G + g) * TC_GATE_ROW_BYTES);
+    row->writers = count;
+    row->ready = std::min<uint64_t>(count / cd.writers, P->round);
+  }
   return TC_OK;
 }
 
@@ -915,6 +949,7 @@ void tc::fill_handle(const tc_plan* P, tc_handle* h) {
   h->gates = (uint64_t)(P->ws + P->L.gates);
   h->gate_stride = P->L.gate_stride;
   h->writers = (uint64_t)(P->ws + P->L.writers);
+  h->marks = (uint64_t)(P->ws + P->L.marks);
   h->round = P->round;
   h->nranks = P->P;
   for (uint32_t p = 0; p <= P->P; ++p) h->chunk_base[p] = P->chunk_base[p];

@@ -18,20 +18,18 @@ constexpr uint32_t kStatusAborted = 1;  // engine stopped by the host's abort wo
 constexpr uint32_t kStatusExpired = 2;  // engine stopped by its wall-clock backstop
 
 // Per-chunk flags written by the completion check.
-constexpr uint32_t kFlagExtra = 1;       // writer counter > round * writers
-constexpr uint32_t kFlagShortMarks = 2;  // writer counter < round * writers
-constexpr uint32_t kFlagNotOpen = 4;     // ready < round
+constexpr uint32_t kFlagExtra = 1;       // mark count > round * writers
+constexpr uint32_t kFlagShortMarks = 2;  // mark count < round * writers (gate not open)
 constexpr uint32_t kFlagNotArrived = 8;  // some receiver's arrival < round
 constexpr uint32_t kFlagCorrupt = 16;    // values no correct run produces
 
 // Byte offsets into the caller's workspace.
 struct Layout {
   uint64_t gates, gate_stride;
-  uint64_t pieces, chunks, writers, wprefix;
+  uint64_t pieces, chunks, writers, marks, wprefix;
   uint64_t launch[2], launch_bytes;     // tickets | stats | stop | done, per launch parity
   uint64_t round_blk[2], round_bytes;   // sig | cursors, per round parity
   uint64_t status;
-  uint64_t check;
   uint64_t total;
 };
 
