@@ -158,7 +158,7 @@ def run_headline(args, torch, tc, workloads, seed):
     return out
 
 
-def run_overlap(torch, tc, workloads, seed, reps=15, cu_mask=None, engine_ctas=0):
+def run_overlap(torch, tc, workloads, seed, reps=40, cu_mask=None, engine_ctas=0):
     """GEMM producer time for P ranks back to back, without any plan and with
     the copy engine delivering each rank's tiles while the next GEMM runs."""
     from synth import gemm_operands
@@ -179,33 +179,26 @@ def run_overlap(torch, tc, workloads, seed, reps=15, cu_mask=None, engine_ctas=0
                          programs=w["programs"], group_m=w["group_m"], handle=h, rank=p,
                          first_chunk=0, tiles_per_chunk=w["tiles_per_chunk"], stream=prod)
 
-    alone = []
-    for i in range(reps + 2):
-        torch.cuda.synchronize()
-        e0.record(prod)
-        gemms(None)
-        e1.record(prod)
-        e1.synchronize()
-        if i >= 2:
-            alone.append(e0.elapsed_time(e1))
-    # The same GEMMs marking a plan's gates with no copy engine running: the
-    # cost of the mark protocol itself (a throwaway plan whose round is never
-    # started).
-    marks_only = []
+    # Three variants, interleaved rep by rep so that clock or placement drift
+    # hits all of them alike: the GEMMs with no plan; the same GEMMs marking
+    # the gates of a throwaway plan whose round is never started (the cost of
+    # the mark protocol alone); and full rounds with the copy engine running.
     scratch = tc.TriggeredPlan(rep, build_sched(w, views, tc), engine_ctas=1)
     h0 = scratch.current_handle()
-    for i in range(reps + 2):
+    plan = tc.TriggeredPlan(rep, build_sched(w, views, tc), cu_mask=cu_mask, engine_ctas=engine_ctas)
+
+    def timed(h):
         torch.cuda.synchronize()
         e0.record(prod)
-        gemms(h0)
+        gemms(h)
         e1.record(prod)
         e1.synchronize()
-        if i >= 2:
-            marks_only.append(e0.elapsed_time(e1))
-    scratch.close()
-    plan = tc.TriggeredPlan(rep, build_sched(w, views, tc), cu_mask=cu_mask, engine_ctas=engine_ctas)
-    over, rounds = [], []
-    for i in range(reps + 2):
+        return e0.elapsed_time(e1)
+
+    alone, marks_only, over, rounds = [], [], [], []
+    for i in range(reps + 3):
+        a_ms = timed(None)
+        m_ms = timed(h0)
         torch.cuda.synchronize()
         a = time.perf_counter()
         h = plan.start(prod)
@@ -215,9 +208,12 @@ def run_overlap(torch, tc, workloads, seed, reps=15, cu_mask=None, engine_ctas=0
         plan.wait(30.0)
         plan.next_round()
         b = time.perf_counter()
-        if i >= 2:
+        if i >= 3:
+            alone.append(a_ms)
+            marks_only.append(m_ms)
             over.append(e0.elapsed_time(e1))
             rounds.append((b - a) * 1e3)
+    scratch.close()
     ectas = plan.stats()["engine_ctas"]
     plan.close()
     flops = 2.0 * M * N * K * P

@@ -145,8 +145,11 @@ class Schedule:
         return self._ptr
 
     def __del__(self):
-        if getattr(self, "_ptr", None) and self._ptr.value and _lib._lib is not None:
-            _lib._lib.tc_schedule_free(self._ptr)
+        # At interpreter exit the module globals may already be gone.
+        lib_mod = globals().get("_lib")
+        if getattr(self, "_ptr", None) and self._ptr.value and lib_mod is not None \
+                and getattr(lib_mod, "_lib", None) is not None:
+            lib_mod._lib.tc_schedule_free(self._ptr)
             self._ptr = C.c_void_p(0)
 
     def tables(self):

@@ -150,6 +150,11 @@ __device__ inline uint32_t wave_add(uint32_t* p, uint32_t v) {
   const uint32_t mine = tc_lane_id() == 0 ? v : 0u;
   return tc_uniform(__hip_atomic_fetch_add(p, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
+// The same without waiting for the result.
+__device__ inline void wave_add_noret(uint32_t* p, uint32_t v) {
+  const uint32_t mine = tc_lane_id() == 0 ? v : 0u;
+  __hip_atomic_fetch_add(p, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ inline uint32_t wave_load(const uint32_t* p) {
   return tc_uniform(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
@@ -183,12 +188,17 @@ __device__ inline bool must_stop(const EngineArgs& a, uint64_t t0, uint32_t spin
   return true;
 }
 
-// Uniform spin until ready() holds.  Waves sleep longer the longer they
-// wait; "reserve" waves (all but one in eight) sleep about 20 us between
-// polls once they have waited a little, so thousands of idle workers put
-// almost no load on the memory system while a producer runs.
+// How a waiting wave backs off between polls.  Gate polls by most waves of a
+// large grid are "reserve" polls: about 20 us between polls once the wave
+// has waited a little, so thousands of idle workers put almost no load on
+// the memory system while a producer runs.  The few waves waiting on another
+// wave of the engine (a chunk's last pieces, its turn to signal) poll
+// briskly: they are on the round's critical path.
+constexpr int kPollNormal = 0, kPollReserve = 1, kPollBrisk = 2;
+
+// Uniform spin until ready() holds.
 template <typename Ready>
-__device__ inline bool poll_until(const EngineArgs& a, uint64_t t0, bool reserve, Ready ready) {
+__device__ inline bool poll_until(const EngineArgs& a, uint64_t t0, int mode, Ready ready) {
   uint32_t spins = 0;
   for (;;) {
     if (ready()) {
@@ -196,9 +206,9 @@ __device__ inline bool poll_until(const EngineArgs& a, uint64_t t0, bool reserve
       return true;
     }
     if (must_stop(a, t0, ++spins)) return false;
-    if (spins < 8) {
-      __builtin_amdgcn_s_sleep(2);
-    } else if (!reserve) {
+    if (spins < 8 || mode == kPollBrisk) {
+      __builtin_amdgcn_s_sleep(1);
+    } else if (mode == kPollNormal) {
       if (spins < 64) __builtin_amdgcn_s_sleep(16);
       else __builtin_amdgcn_s_sleep(64);
     } else {
@@ -227,22 +237,24 @@ __device__ inline tc_gate_row* gate_row(const EngineArgs& a, uint32_t table, uin
 // Signal chunk `c` (global id g) of source p once every earlier chunk of p
 // has been signalled.  Every piece's stores completed (at system scope)
 // before its `done` increment, so the bytes are visible when this runs.
+// The engine is the only writer of arrival counters and signals each chunk
+// once per round, so the increment is a plain store of the round (a store
+// completes in a fraction of the time an atomic takes).
 __device__ bool signal_in_order(const EngineArgs& a, uint32_t p, uint32_t c, uint32_t g,
                                 uint64_t t0) {
   uint32_t* sig = a.sig + p * kTicketStride;
   uint32_t seen = 0;
-  if (!poll_until(a, t0, false, [&] { return (seen = wave_load_sys(sig)) >= c; })) return false;
+  if (!poll_until(a, t0, kPollBrisk, [&] { return (seen = wave_load_sys(sig)) >= c; })) return false;
   if (seen > c) return true;  // signalled by an earlier launch of this round
-  const uint64_t one = tc_lane_id() == 0 ? 1u : 0u;
   for (uint32_t q = 0; q < a.nranks; ++q) {
     if (q == p) continue;
-    __hip_atomic_fetch_add(&gate_row(a, q, g)->arrival, one, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(&gate_row(a, q, g)->arrival, (uint64_t)a.round, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_SYSTEM);
     __hip_atomic_store(a.cur + p * a.nranks + q, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
-  wave_max32(&a.stats[1], (uint32_t)now_ticks());
   wave_wait_stores();  // this chunk's arrivals land before the next chunk may signal
   __hip_atomic_store(sig, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  wave_max32(&a.stats[1], (uint32_t)now_ticks());
   return true;
 }
 
@@ -347,7 +359,7 @@ __global__ __launch_bounds__(kEngineThreads) void engine_kernel(EngineArgs a) {
   uint32_t acquired = 0xFFFFFFFFu;  // last chunk whose gate this wave has seen open
   // Large grids keep one wave in eight polling briskly and let the rest back
   // off; small grids poll with every wave.
-  const bool reserve = gridDim.x >= 256 && gw % 8 != 0;
+  const int gate_mode = gridDim.x >= 256 && gw % 8 != 0 ? kPollReserve : kPollNormal;
 
   for (uint32_t s = 0; s < a.nranks; ++s) {
     const uint32_t p = (gw + s) % a.nranks;
@@ -361,7 +373,7 @@ __global__ __launch_bounds__(kEngineThreads) void engine_kernel(EngineArgs a) {
       if (g != acquired) {
         // The gate of round r is open once the chunk's marks reach r * writers.
         const uint64_t want = (uint64_t)a.round * tc_uniform(a.chunks[g].writers);
-        if (!poll_until(a, t0, reserve, [&] { return mark_count(a, g) >= want; })) return;
+        if (!poll_until(a, t0, gate_mode, [&] { return mark_count(a, g) >= want; })) return;
         // The wave holding a chunk's first piece records when it saw the gate open.
         if (a.piece_base[p] + t == a.chunks[g].first_piece) wave_max32(&a.stats[0], ~(uint32_t)now_ticks());
         acquired = g;
@@ -371,9 +383,17 @@ __global__ __launch_bounds__(kEngineThreads) void engine_kernel(EngineArgs a) {
       else
         copy_2d(a, p, pc);
       wave_wait_stores();  // this piece's bytes are visible at system scope
+      // The wave holding a chunk's last piece signals the chunk once the
+      // other pieces are counted done; the others count theirs and move on
+      // without waiting for the atomic's result.
       const ChunkD cd = a.chunks[g];
-      const uint32_t old = wave_add(a.done + (uint64_t)g * kTicketStride, 1u);
-      if (old + 1 == cd.npieces && !signal_in_order(a, p, cd.local, g, t0)) return;
+      uint32_t* done = a.done + (uint64_t)g * kTicketStride;
+      if (a.piece_base[p] + t + 1 != cd.first_piece + cd.npieces) {
+        wave_add_noret(done, 1u);
+        continue;
+      }
+      if (!poll_until(a, t0, kPollBrisk, [&] { return wave_load(done) + 1 >= cd.npieces; })) return;
+      if (!signal_in_order(a, p, cd.local, g, t0)) return;
     }
   }
 }
@@ -386,30 +406,22 @@ struct CheckArgs {
   uint32_t* flags;        // mapped pinned host memory, one word per chunk
   uint32_t* status;       // device engine status word: read, reported, cleared
   uint32_t* status_host;  // mapped pinned host memory
-  uint32_t G, nranks, round, pad;
+  uint32_t* seq_host;     // mapped pinned host memory: `seq` once every flag is written
+  uint32_t G, nranks, round, seq;
 };
+
+constexpr int kCheckThreads = 1024;
 
 __device__ inline uint64_t ld(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// One thread per global chunk: compare its counters with what a complete
-// round r leaves ([TP] Gates and rounds: this rank's chunk marked by all its
-// writers and arrived at every peer).
-__global__ void check_kernel(CheckArgs a) {
-  const uint32_t g = blockIdx.x * blockDim.x + threadIdx.x;
-  if (g == 0) {  // hand the engine's status to the host and clear it for the next launch
-    const uint32_t st = __hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    __hip_atomic_store(a.status_host, st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    __hip_atomic_store(a.status, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  }
-  if (g >= a.G) return;
+// Flags of global chunk g: its counters against what a complete round r
+// leaves ([TP] Gates and rounds: this rank's chunk marked by all its writers
+// and arrived at every peer).
+__device__ uint32_t check_chunk(const CheckArgs& a, uint32_t g) {
   const ChunkD cd = a.chunks[g];
   const uint64_t want = (uint64_t)a.round * cd.writers;
-  auto row = [&](uint32_t q) {
-    return reinterpret_cast<const tc_gate_row*>(a.gates + (uint64_t)q * a.gate_stride +
-                                                (uint64_t)g * TC_GATE_ROW_BYTES);
-  };
   uint64_t marks = 0;
   for (uint32_t k = 0; k < TC_MARK_STRIPES; ++k)
     marks += ld(reinterpret_cast<const uint64_t*>(
@@ -418,7 +430,8 @@ __global__ void check_kernel(CheckArgs a) {
   if (marks > want) f |= kFlagExtra;
   if (marks < want) f |= kFlagShortMarks;
   for (uint32_t q = 0; q < a.nranks; ++q) {
-    const tc_gate_row* r = row(q);
+    const tc_gate_row* r = reinterpret_cast<const tc_gate_row*>(
+        a.gates + (uint64_t)q * a.gate_stride + (uint64_t)g * TC_GATE_ROW_BYTES);
     for (int k = 0; k < 5; ++k)
       if (ld(&r->rsvd[k]) != 0) f |= kFlagCorrupt;
     if (ld(&r->ready) != 0 || ld(&r->writers) != 0) f |= kFlagCorrupt;
@@ -430,7 +443,23 @@ __global__ void check_kernel(CheckArgs a) {
     if (arr < a.round) f |= kFlagNotArrived;
     if (arr > a.round) f |= kFlagCorrupt;
   }
-  __hip_atomic_store(a.flags + g, f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  return f;
+}
+
+// One CTA: every chunk's flags into host memory, the engine's status handed
+// over (and cleared for the next launch), then the sequence number the host
+// waits for.
+__global__ __launch_bounds__(kCheckThreads) void check_kernel(CheckArgs a) {
+  for (uint32_t g = threadIdx.x; g < a.G; g += kCheckThreads)
+    __hip_atomic_store(a.flags + g, check_chunk(a, g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  if (threadIdx.x == 0) {
+    const uint32_t st = __hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(a.status_host, st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(a.status, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_store(a.seq_host, a.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 }  // namespace
@@ -510,6 +539,11 @@ static int launch_engine(tc_plan* P) {
   a.backstop_ticks = P->backstop_ticks;
   P->cur_launch_block = lb;
   P->launch_seq++;
+  if (P->engine_ms_pending) {  // read the previous launch's time before its events are reused
+    TC_HIP(hipEventSynchronize(P->ev_engine_done));
+    TC_HIP(hipEventElapsedTime(&P->last_engine_ms, P->ev_engine_start, P->ev_engine_done));
+    P->engine_ms_pending = false;
+  }
   TC_HIP(hipEventRecord(P->ev_engine_start, P->engine_stream));
   hipLaunchKernelGGL(engine_kernel, dim3(P->engine_ctas), dim3(kEngineThreads), 0, P->engine_stream, a);
   TC_HIP(hipGetLastError());
@@ -532,13 +566,14 @@ static int queue_check(tc_plan* P) {
   c.flags = P->flags_dev;
   c.status = reinterpret_cast<uint32_t*>(P->ws + P->L.status);
   c.status_host = P->status_dev;
+  c.seq_host = P->seq_dev;
   c.G = P->G;
   c.nranks = P->P;
   c.round = P->round;
-  const uint32_t blocks = std::max<uint32_t>(1, (P->G + 255) / 256);
-  hipLaunchKernelGGL(check_kernel, dim3(blocks), dim3(256), 0, P->engine_stream, c);
+  c.seq = ++P->check_seq;
+  hipLaunchKernelGGL(check_kernel, dim3(1), dim3(kCheckThreads), 0, P->engine_stream, c);
   TC_HIP(hipGetLastError());
-  TC_HIP(hipEventRecord(P->ev_check_done, P->engine_stream));
+  TC_HIP(hipEventRecord(P->ev_check_done, P->engine_stream));  // for close()
   return TC_OK;
 }
 
@@ -555,6 +590,18 @@ static int event_done_by(hipEvent_t ev, std::chrono::steady_clock::time_point de
     }
     if (std::chrono::steady_clock::now() >= deadline) return 0;
     if (++spins > 2000) std::this_thread::sleep_for(std::chrono::microseconds(20));
+  }
+}
+
+// Spins until the check kernel has published sequence number `seq`, or the
+// deadline passes.  1 = done, 0 = deadline.
+static int check_done_by(const tc_plan* P, uint32_t seq,
+                         std::chrono::steady_clock::time_point deadline) {
+  int spins = 0;
+  for (;;) {
+    if (__atomic_load_n(P->seq_host, __ATOMIC_ACQUIRE) == seq) return 1;
+    if (std::chrono::steady_clock::now() >= deadline) return 0;
+    if (++spins > 20000) std::this_thread::sleep_for(std::chrono::microseconds(20));
   }
 }
 
@@ -603,6 +650,7 @@ static void destroy(tc_plan* P) {
   if (P->abort_host) (void)hipHostFree((void*)P->abort_host);
   if (P->flags_host) (void)hipHostFree(P->flags_host);
   if (P->status_host) (void)hipHostFree(P->status_host);
+  if (P->seq_host) (void)hipHostFree((void*)P->seq_host);
   delete P;
 }
 
@@ -678,6 +726,9 @@ int tc_plan_create(const tc_plan_desc* d, tc_plan** out) {
   TC_HIP_C(hipHostGetDevicePointer((void**)&P->flags_dev, P->flags_host, 0));
   TC_HIP_C(hipHostMalloc((void**)&P->status_host, 64, hipHostMallocMapped | hipHostMallocCoherent));
   TC_HIP_C(hipHostGetDevicePointer((void**)&P->status_dev, P->status_host, 0));
+  TC_HIP_C(hipHostMalloc((void**)&P->seq_host, 64, hipHostMallocMapped | hipHostMallocCoherent));
+  *P->seq_host = 0;
+  TC_HIP_C(hipHostGetDevicePointer((void**)&P->seq_dev, (void*)P->seq_host, 0));
 
   // Zero the workspace (gates start at zero, [TP] Gates and rounds), then
   // upload the descriptors once.
@@ -762,25 +813,21 @@ int tc_plan_wait(tc_plan* P, uint64_t timeout_us) {
   // the producer's work, so extra marks issued after the gate opened count.
   if (int rc = queue_check(P)) return rc;
   const auto deadline = std::chrono::steady_clock::now() + std::chrono::microseconds(timeout_us);
-  hipError_t err = hipSuccess;
-  const int done = event_done_by(P->ev_check_done, deadline, &err);
-  if (done < 0) return hip_fail(err, "hipEventQuery");
-  const bool timed_out = done == 0;
+  const uint32_t seq = P->check_seq;
+  const bool timed_out = check_done_by(P, seq, deadline) == 0;
   if (timed_out) {
     // Stop this launch of the engine if it still runs (every poll loop
     // watches the abort word), then let the queued check finish.
     if (hipEventQuery(P->ev_engine_done) != hipSuccess)
       __atomic_store_n(P->abort_host, P->launch_id, __ATOMIC_SEQ_CST);
     const auto drain = std::chrono::steady_clock::now() + std::chrono::seconds(10);
-    const int e3 = event_done_by(P->ev_check_done, drain, &err);
-    if (e3 < 0) return hip_fail(err, "hipEventQuery");
-    if (e3 == 0) {
+    if (check_done_by(P, seq, drain) == 0) {
       P->need_relaunch = hipEventQuery(P->ev_engine_done) == hipSuccess;
       return fail(TC_ETIMEOUT, "wait: the copy engine or the producer did not finish within 10 s "
                                "of the deadline");
     }
   }
-  TC_HIP(hipEventElapsedTime(&P->last_engine_ms, P->ev_engine_start, P->ev_engine_done));
+  P->engine_ms_pending = true;
   const uint32_t st = __atomic_load_n(P->status_host, __ATOMIC_ACQUIRE);
   if (st & (kStatusAborted | kStatusExpired)) P->need_relaunch = true;
   bool extra = false, corrupt = false, shortc = false;
@@ -841,10 +888,11 @@ int tc_plan_close(tc_plan* P) {
     __atomic_store_n(P->abort_host, P->launch_id, __ATOMIC_SEQ_CST);
     hipError_t err = hipSuccess;
     const auto drain = std::chrono::steady_clock::now() + std::chrono::seconds(10);
-    if (event_done_by(P->ev_engine_done, drain, &err) != 1)
+    // The engine stream may be shared with other plans: wait for this plan's
+    // own work only.
+    if (event_done_by(P->ev_engine_done, drain, &err) != 1 ||
+        (P->check_seq && event_done_by(P->ev_check_done, drain, &err) != 1))
       rc = fail(TC_ETIMEOUT, "close: copy engine did not stop within 10 s");
-    else
-      (void)hipStreamSynchronize(P->engine_stream);
   }
   if (rc == TC_OK) destroy(P);  // on failure leak rather than free memory a kernel may touch
   return rc;
@@ -909,6 +957,11 @@ int tc_plan_read_cursors(tc_plan* P, uint32_t* host) {
 int tc_plan_stats(tc_plan* P, tc_stats* out) {
   if (!P || !out) return fail(TC_EINVAL, "stats: NULL argument");
   std::memset(out, 0, sizeof(*out));
+  if (P->engine_ms_pending) {  // the engine's events are complete once wait() saw the check
+    TC_HIP(hipEventSynchronize(P->ev_engine_done));
+    TC_HIP(hipEventElapsedTime(&P->last_engine_ms, P->ev_engine_start, P->ev_engine_done));
+    P->engine_ms_pending = false;
+  }
   out->engine_ms = P->last_engine_ms;
   out->launches = P->launches_this_round;
   out->engine_ctas = P->engine_ctas;

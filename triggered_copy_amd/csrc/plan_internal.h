@@ -63,6 +63,9 @@ struct tc_plan {
   uint32_t* flags_dev = nullptr;
   uint32_t* status_host = nullptr;          // pinned, mapped: engine status of the last launch
   uint32_t* status_dev = nullptr;
+  volatile uint32_t* seq_host = nullptr;    // pinned, mapped: the last check's sequence number
+  uint32_t* seq_dev = nullptr;
+  uint32_t check_seq = 0;
 
   uint32_t engine_ctas = 0;
   uint64_t backstop_ticks = 0;
@@ -74,6 +77,7 @@ struct tc_plan {
   uint32_t launches_this_round = 0;
   bool need_relaunch = false;
   float last_engine_ms = 0.f;
+  bool engine_ms_pending = false;  // last_engine_ms not yet read from the events
   std::vector<uint32_t> problems;  // (rank, chunk) pairs
 };
 
