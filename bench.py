@@ -229,6 +229,37 @@ def run_overlap(torch, tc, workloads, seed, reps=40, cu_mask=None, engine_ctas=0
                 delivered_gbs=P * (P - 1) * (B // P) / (statistics.median(rounds) * 1e-3) / 1e9)
 
 
+def run_gemm_only(torch, tc, workloads, seed, reps):
+    """The P GEMM producers back to back with no plan, `reps` times."""
+    from synth import gemm_operands
+    import numpy as np
+    w = workloads.FULL["gemm_tiles_p4"]
+    P, M, N, K = w["P"], w["rows"], w["cols"], w["K"]
+    ops = []
+    for p in range(P):
+        a, bt = gemm_operands(seed, p, 1, M, N, K)
+        ops.append((torch.from_numpy(a.view(np.int16)).cuda(), torch.from_numpy(bt.view(np.int16)).cuda()))
+    out = torch.zeros(P * M * N, dtype=torch.int16, device="cuda")
+    prod = torch.cuda.Stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for i in range(reps + 2):
+        torch.cuda.synchronize()
+        e0.record(prod)
+        for p in range(P):
+            tc.gemm_bf16(ops[p][0], ops[p][1], out[p * M * N:], ldc=N, M=M, N=N,
+                         programs=w["programs"], group_m=w["group_m"], stream=prod)
+        e1.record(prod)
+        e1.synchronize()
+        if i >= 2:
+            ts.append(e0.elapsed_time(e1))
+    ms = statistics.median(ts)
+    flops = 2.0 * M * N * K * P
+    return {"metric": "bf16 GEMM producer (M=N=2000, K=1024, 4 ranks back to back)",
+            "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+            "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "reps": reps}
+
+
 def run_barrier(torch, tc, workloads):
     w = workloads.FULL["barrier_p8"]
     P, G = w["P"], w["gens"]
@@ -312,6 +343,11 @@ def main():
     ap.add_argument("--engine-ctas", type=int, default=0)
     ap.add_argument("--piece-bytes", type=int, default=0)
     ap.add_argument("--overlap-engine-ctas", type=int, default=0)
+    ap.add_argument("--overlap-cus", type=int, default=0,
+                    help="confine the copy engine of the GEMM overlap run to the first N CUs "
+                         "(0: every CU, shared with the producer)")
+    ap.add_argument("--gemm-only", action="store_true",
+                    help="time only the 4 GEMM producers, with no plan (for counter collection)")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--premark", action="store_true",
                     help="issue the marks before start() (for counter collection)")
@@ -331,6 +367,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     tc.lib()
+    if args.gemm_only:
+        print(json.dumps(run_gemm_only(torch, tc, workloads, BASE_SEED, args.steps)), flush=True)
+        return
 
     if args.calibrate:
         x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
@@ -345,8 +384,15 @@ def main():
     extras = {}
     if not args.no_extras:
         log("overlap: 4 GEMM producers with and without the copy engine")
-        extras["gemm_overlap"] = run_overlap(torch, tc, workloads, BASE_SEED,
+        mask = None
+        if args.overlap_cus:
+            ncu = torch.cuda.get_device_properties(0).multi_processor_count
+            mask = [0] * ((ncu + 31) // 32)
+            for i in range(min(args.overlap_cus, ncu)):
+                mask[i // 32] |= 1 << (i % 32)
+        extras["gemm_overlap"] = run_overlap(torch, tc, workloads, BASE_SEED, cu_mask=mask,
                                              engine_ctas=args.overlap_engine_ctas)
+        extras["gemm_overlap"]["engine_cus"] = args.overlap_cus or "all"
         log("barrier: 8 ranks x 1000 generations")
         extras["barrier_p8"] = run_barrier(torch, tc, workloads)
         log("small rounds")

@@ -359,7 +359,10 @@ int tc_mark(tc_plan* plan, const tc_handle* h, uint32_t rank, uint32_t chunk,
  * accumulate, bf16 out (round to nearest even), C row stride ldc elements.
  * 128x128 tiles; program p takes steps p, p + programs, ...; step s computes
  * tile tc_tile_of(s, tm, tn, group_m) and, when h != NULL, then marks chunk
- * first_chunk + s / tiles_per_chunk of rank `rank`.  A, Bt, C device.
+ * first_chunk + s / tiles_per_chunk of rank `rank`.  When programs is a
+ * multiple of 8, consecutive programs run on one XCD (workgroups are dealt
+ * to the XCDs round-robin), so each XCD's L2 serves a compact block of
+ * tiles.  A, Bt, C device.
  * C is stored with system-scope write-through stores, so its marks need no
  * L2 write-back (tc_mark_ready_wt).
  * TC_EINVAL unless K % 8 == 0, N % 8 == 0, ldc % 8 == 0, ldc < 2^23, pointers

@@ -13,11 +13,12 @@
 //
 // gfx950 mapping: a 256-thread CTA computes a 128 x 128 tile; its 4 waves
 // form a 2 x 2 grid of 64 x 64 sub-tiles, each 4 x 4 blocks of the 16x16x32
-// bf16 MFMA (v_mfma_f32_16x16x32_bf16).  K advances 64 at a time: the next
-// A/B slab is fetched from global memory into registers while the current
-// one is multiplied out of LDS.  LDS rows are padded by 16 bytes to spread
-// the 16-byte fragment reads over the banks.  The finished tile is staged
-// through LDS so the bf16 stores are 16-byte vectors along the row.
+// bf16 MFMA (v_mfma_f32_16x16x32_bf16).  K advances 128 at a time through two
+// LDS buffers: while the waves multiply slab k out of one buffer, slab k + 1
+// is on its way from global memory into registers and then into the other
+// buffer, so one barrier per slab suffices.  LDS rows are padded by 16 bytes
+// to spread the 16-byte fragment reads over the banks.  The finished tile is
+// staged through LDS so the bf16 stores are 16-byte vectors along the row.
 #include <hip/hip_runtime.h>
 
 #include <string>
@@ -35,8 +36,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDA = BK + 8;            // bf16 elements per LDS row (144 bytes)
+constexpr int BM = 128, BN = 128, BK = 128;
+constexpr int LDA = BK + 8;            // bf16 elements per LDS row (16 bytes of padding)
 constexpr int kThreads = 256;
 constexpr int LDC = BN + 8;            // bf16 elements per staged C row
 
@@ -58,19 +59,27 @@ __device__ inline uint32_t f32_to_bf16_rne(float f) {
 }
 
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
-  // One LDS area: A and B slabs during the K loop, the C tile afterwards.
-  constexpr int kSlab = BM * LDA;  // bf16 elements per operand slab
-  static_assert(2 * kSlab >= BM * LDC, "C staging fits in the operand area");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kSlab];
-  uint16_t* As = lds;
-  uint16_t* Bs = lds + kSlab;
+  // Two buffers of (A slab, B slab) during the K loop; the C tile afterwards.
+  constexpr int kSlab = BM * LDA;        // bf16 elements per operand slab
+  constexpr int kVecPerRow = BK / 8;     // 16-byte vectors per slab row
+  constexpr int kVec = BM * kVecPerRow / kThreads;  // vectors per thread per operand
+  static_assert(BM == BN && BM * kVecPerRow % kThreads == 0, "slab vectors split evenly");
+  static_assert(4 * kSlab >= BM * LDC, "C staging fits in the operand area");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kSlab];
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63, wave = tid >> 6;
   const uint32_t wm = wave >> 1, wn = wave & 1;
   const uint32_t nk = (a.K + BK - 1) / BK;
 
-  for (uint32_t step = blockIdx.x; step < a.tiles; step += gridDim.x) {
+  // Workgroups are dealt to the 8 XCDs round-robin; program p of the
+  // persistent grid is workgroup w(p) such that each XCD runs consecutive
+  // programs, hence consecutive steps: a compact block of tiles in the
+  // grouped order, whose A and B panels its L2 shares.  A bijection on
+  // [0, gridDim.x); every step is still taken exactly once.
+  const uint32_t first = gridDim.x % 8 == 0 ? (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8
+                                            : blockIdx.x;
+  for (uint32_t step = first; step < a.tiles; step += gridDim.x) {
     const uint32_t t = tc_tile_of(step, a.tm, a.tn, a.group_m);
     const uint32_t m0 = (t / a.tn) * BM, n0 = (t % a.tn) * BN;
 
@@ -80,15 +89,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Each thread moves 4 16-byte vectors of A and 4 of Bt per K slab:
-    // vector v = tid + 256 * s covers row v / 8, k columns 8 * (v % 8) .. +7.
-    u32x4 ra[4], rb[4];
+    // Vector v = tid + 256 * s of a slab covers row v / kVecPerRow, k columns
+    // 8 * (v % kVecPerRow) .. +7; rows and k past the matrix read as zero.
+    u32x4 ra[kVec], rb[kVec];
     auto fetch = [&](uint32_t kt) {
       const uint32_t k0 = kt * BK;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < kVec; ++s) {
         const uint32_t v = tid + kThreads * s;
-        const uint32_t r = v >> 3, kc = k0 + (v & 7) * 8;
+        const uint32_t r = v / kVecPerRow, kc = k0 + (v % kVecPerRow) * 8;
         const bool kin = kc < a.K;
         ra[s] = (m0 + r < a.M && kin)
                     ? *reinterpret_cast<const u32x4*>(a.A + (uint64_t)(m0 + r) * a.K + kc)
@@ -98,18 +107,27 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
                     : u32x4{0, 0, 0, 0};
       }
     };
-    fetch(0);
-    for (uint32_t kt = 0; kt < nk; ++kt) {
-      __syncthreads();  // the previous slab is no longer being read
+    auto stash = [&](uint32_t buf) {
+      uint16_t* As = lds + buf * 2 * kSlab;
+      uint16_t* Bs = As + kSlab;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < kVec; ++s) {
         const uint32_t v = tid + kThreads * s;
-        const uint32_t r = v >> 3, c = (v & 7) * 8;
+        const uint32_t r = v / kVecPerRow, c = (v % kVecPerRow) * 8;
         *reinterpret_cast<u32x4*>(As + r * LDA + c) = ra[s];
         *reinterpret_cast<u32x4*>(Bs + r * LDA + c) = rb[s];
       }
-      __syncthreads();
+    };
+
+    __syncthreads();  // the previous tile's C staging is no longer being read
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (uint32_t kt = 0; kt < nk; ++kt) {
+      const uint32_t cur = kt & 1;
       if (kt + 1 < nk) fetch(kt + 1);  // in flight while this slab is multiplied
+      const uint16_t* As = lds + cur * 2 * kSlab;
+      const uint16_t* Bs = As + kSlab;
 #pragma unroll
       for (int kk = 0; kk < BK; kk += 32) {
         // Operand fragment of one 16x16x32 block: lane l holds row (l % 16)
@@ -128,11 +146,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
           for (int j = 0; j < 4; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
       }
+      // The other buffer was last read in the previous iteration, which every
+      // wave finished before that iteration's closing barrier.
+      if (kt + 1 < nk) stash(cur ^ 1);
+      __syncthreads();
     }
 
-    // Stage the tile as bf16 in LDS.  Output block layout: lane l holds rows
+    // Stage the tile as bf16 in LDS (the loop's closing barrier ends every
+    // read of the operand buffers).  Output block layout: lane l holds rows
     // 4 * (l / 16) + e, e = 0..3, of column l % 16.
-    __syncthreads();
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
