@@ -11,14 +11,18 @@
 // operands stream along K), bf16 inputs, fp32 accumulation on the matrix
 // cores, bf16 output (round to nearest even).
 //
-// gfx950 mapping: a 256-thread CTA computes a 128 x 128 tile; its 4 waves
-// form a 2 x 2 grid of 64 x 64 sub-tiles, each 4 x 4 blocks of the 16x16x32
-// bf16 MFMA (v_mfma_f32_16x16x32_bf16).  K advances 128 at a time through two
-// LDS buffers: while the waves multiply slab k out of one buffer, slab k + 1
-// is on its way from global memory into registers and then into the other
-// buffer, so one barrier per slab suffices.  LDS rows are padded by 16 bytes
-// to spread the 16-byte fragment reads over the banks.  The finished tile is
-// staged through LDS so the bf16 stores are 16-byte vectors along the row.
+// gfx950 mapping: a 512-thread CTA computes a 128 x 128 tile with two groups
+// of 4 waves.  In each group the waves form a 2 x 2 grid of 64 x 64
+// sub-tiles, each 4 x 4 blocks of the 16x16x32 bf16 MFMA
+// (v_mfma_f32_16x16x32_bf16).  The groups split K: group g multiplies the
+// 64-wide slabs g, g + 2, g + 4, ..., each through two LDS buffers of its
+// own (slab k + 2 travels from global memory into registers and then into
+// the other buffer while slab k is multiplied).  Two waves per SIMD, one of
+// each group, so one wave's MFMAs cover the other's load and LDS latency.
+// At the end group 1 hands its partial sums to group 0 through LDS.  LDS
+// rows are padded by 16 bytes to spread the 16-byte fragment reads over the
+// banks; the finished tile is staged through LDS so the bf16 stores are
+// 16-byte vectors along the row.
 #include <hip/hip_runtime.h>
 
 #include <string>
@@ -36,9 +40,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BN = 128, BK = 128;
+constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int LDA = BK + 8;            // bf16 elements per LDS row (16 bytes of padding)
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;          // two groups of 4 waves
+constexpr int kGroupThreads = 256;
 constexpr int LDC = BN + 8;            // bf16 elements per staged C row
 
 struct GemmArgs {
@@ -59,18 +64,27 @@ __device__ inline uint32_t f32_to_bf16_rne(float f) {
 }
 
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
-  // Two buffers of (A slab, B slab) during the K loop; the C tile afterwards.
+  // LDS: slab (group g, buffer b, operand o) at (4 g + 2 b + o) * kSlab during
+  // the K loop; afterwards group 1's partial sums (kRed floats) followed by
+  // the staged C tile.
   constexpr int kSlab = BM * LDA;        // bf16 elements per operand slab
   constexpr int kVecPerRow = BK / 8;     // 16-byte vectors per slab row
-  constexpr int kVec = BM * kVecPerRow / kThreads;  // vectors per thread per operand
-  static_assert(BM == BN && BM * kVecPerRow % kThreads == 0, "slab vectors split evenly");
-  static_assert(4 * kSlab >= BM * LDC, "C staging fits in the operand area");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kSlab];
+  constexpr int kVec = BM * kVecPerRow / kGroupThreads;  // vectors per thread per operand
+  constexpr int kRed = 4 * 64 * 64;      // floats: 4 waves x 64 lanes x 64 accumulators
+  static_assert(BM == BN && BM * kVecPerRow % kGroupThreads == 0, "slab vectors split evenly");
+  static_assert(8 * kSlab * 2 >= kRed * 4 + BM * LDC * 2, "reduction and C staging fit");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[8 * kSlab];
+  float* red = reinterpret_cast<float*>(lds);
+  uint16_t* cst = lds + kRed * 2;
 
   const uint32_t tid = threadIdx.x;
-  const uint32_t lane = tid & 63, wave = tid >> 6;
-  const uint32_t wm = wave >> 1, wn = wave & 1;
+  const uint32_t lane = tid & 63;
+  const uint32_t grp = tc_uniform(tid >> 8);           // K group, wave-uniform
+  const uint32_t gw = tc_uniform((tid >> 6) & 3);      // wave within the group
+  const uint32_t gtid = tid & (kGroupThreads - 1);
+  const uint32_t wm = gw >> 1, wn = gw & 1;
   const uint32_t nk = (a.K + BK - 1) / BK;
+  const uint32_t niter = (nk + 1) / 2;                 // slabs per group, rounded up
 
   // Workgroups are dealt to the 8 XCDs round-robin; program p of the
   // persistent grid is workgroup w(p) such that each XCD runs consecutive
@@ -89,14 +103,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Vector v = tid + 256 * s of a slab covers row v / kVecPerRow, k columns
-    // 8 * (v % kVecPerRow) .. +7; rows and k past the matrix read as zero.
+    // Vector v = gtid + 256 * s of a slab covers row v / kVecPerRow, k
+    // columns 8 * (v % kVecPerRow) .. +7; rows and k past the matrix read
+    // as zero.
     u32x4 ra[kVec], rb[kVec];
     auto fetch = [&](uint32_t kt) {
       const uint32_t k0 = kt * BK;
 #pragma unroll
       for (int s = 0; s < kVec; ++s) {
-        const uint32_t v = tid + kThreads * s;
+        const uint32_t v = gtid + kGroupThreads * s;
         const uint32_t r = v / kVecPerRow, kc = k0 + (v % kVecPerRow) * 8;
         const bool kin = kc < a.K;
         ra[s] = (m0 + r < a.M && kin)
@@ -107,66 +122,86 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
                     : u32x4{0, 0, 0, 0};
       }
     };
+    auto slab = [&](uint32_t buf) { return lds + (4 * grp + 2 * buf) * kSlab; };
     auto stash = [&](uint32_t buf) {
-      uint16_t* As = lds + buf * 2 * kSlab;
+      uint16_t* As = slab(buf);
       uint16_t* Bs = As + kSlab;
 #pragma unroll
       for (int s = 0; s < kVec; ++s) {
-        const uint32_t v = tid + kThreads * s;
+        const uint32_t v = gtid + kGroupThreads * s;
         const uint32_t r = v / kVecPerRow, c = (v % kVecPerRow) * 8;
         *reinterpret_cast<u32x4*>(As + r * LDA + c) = ra[s];
         *reinterpret_cast<u32x4*>(Bs + r * LDA + c) = rb[s];
       }
     };
 
-    __syncthreads();  // the previous tile's C staging is no longer being read
-    fetch(0);
-    stash(0);
+    __syncthreads();  // the previous tile's partial sums and C staging are no longer read
+    if (grp < nk) {
+      fetch(grp);
+      stash(0);
+    }
     __syncthreads();
-    for (uint32_t kt = 0; kt < nk; ++kt) {
-      const uint32_t cur = kt & 1;
-      if (kt + 1 < nk) fetch(kt + 1);  // in flight while this slab is multiplied
-      const uint16_t* As = lds + cur * 2 * kSlab;
-      const uint16_t* Bs = As + kSlab;
+    // Every wave passes the same barriers: a group without a slab in some
+    // iteration (odd slab counts) skips the work, not the barrier.
+    for (uint32_t it = 0; it < niter; ++it) {
+      const uint32_t kt = 2 * it + grp, cur = it & 1;
+      if (kt + 2 < nk) fetch(kt + 2);  // in flight while this slab is multiplied
+      if (kt < nk) {
+        const uint16_t* As = slab(cur);
+        const uint16_t* Bs = As + kSlab;
 #pragma unroll
-      for (int kk = 0; kk < BK; kk += 32) {
-        // Operand fragment of one 16x16x32 block: lane l holds row (l % 16)
-        // and 8 consecutive k values starting at 8 * (l / 16).
-        const uint32_t fr = lane & 15, fk = kk + 8 * (lane >> 4);
-        bf16x8 fa[4], fb[4];
+        for (int kk = 0; kk < BK; kk += 32) {
+          // Operand fragment of one 16x16x32 block: lane l holds row
+          // (l % 16) and 8 consecutive k values starting at 8 * (l / 16).
+          const uint32_t fr = lane & 15, fk = kk + 8 * (lane >> 4);
+          bf16x8 fa[4], fb[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          fa[i] = *reinterpret_cast<const bf16x8*>(As + (wm * 64 + i * 16 + fr) * LDA + fk);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          fb[j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 64 + j * 16 + fr) * LDA + fk);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i)
+            fa[i] = *reinterpret_cast<const bf16x8*>(As + (wm * 64 + i * 16 + fr) * LDA + fk);
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            fb[j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 64 + j * 16 + fr) * LDA + fk);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
       }
       // The other buffer was last read in the previous iteration, which every
       // wave finished before that iteration's closing barrier.
-      if (kt + 1 < nk) stash(cur ^ 1);
+      if (kt + 2 < nk) stash(cur ^ 1);
       __syncthreads();
     }
 
-    // Stage the tile as bf16 in LDS (the loop's closing barrier ends every
-    // read of the operand buffers).  Output block layout: lane l holds rows
-    // 4 * (l / 16) + e, e = 0..3, of column l % 16.
+    // Group 1's partial sums to LDS, in the same fragment order group 0's
+    // wave of the same (wm, wn) holds them.
+    if (grp == 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t r = wm * 64 + i * 16 + 4 * (lane >> 4) + e;
-          const uint32_t c = wn * 64 + j * 16 + (lane & 15);
-          lds[r * LDC + c] = (uint16_t)f32_to_bf16_rne(acc[i][j][e]);
-        }
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<f32x4*>(red + ((gw * 16 + i * 4 + j) * 64 + lane) * 4) = acc[i][j];
+    }
     __syncthreads();
-    // 128 rows x 16 vectors of 8 bf16: 8 vectors per thread, stored through
+    // Group 0 adds them and stages the tile as bf16.  Output block layout:
+    // lane l holds rows 4 * (l / 16) + e, e = 0..3, of column l % 16.
+    if (grp == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 o = *reinterpret_cast<const f32x4*>(red + ((gw * 16 + i * 4 + j) * 64 + lane) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t r = wm * 64 + i * 16 + 4 * (lane >> 4) + e;
+            const uint32_t c = wn * 64 + j * 16 + (lane & 15);
+            cst[r * LDC + c] = (uint16_t)f32_to_bf16_rne(acc[i][j][e] + o[e]);
+          }
+        }
+    }
+    __syncthreads();
+    // 128 rows x 16 vectors of 8 bf16: 4 vectors per thread, stored through
     // to memory at system scope, so that once they complete the tile is
     // visible everywhere and mark_ready needs no L2 write-back.  Lanes
     // outside the matrix get an offset past the buffer range and their
@@ -177,12 +212,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
     const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
         a.C + (uint64_t)m0 * a.ldc + n0, 0, (int)extent, 0x00020000);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < BM * BN / 8 / kThreads; ++s) {
       const uint32_t v = tid + kThreads * s;
       const uint32_t r = v >> 4, c = (v & 15) * 8;
       const bool in = r < rows_in && c < cols_in;
       const uint32_t off = in ? (uint32_t)(((uint64_t)r * a.ldc + c) * 2) : 0xFFFFFFF0u;
-      __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(lds + r * LDC + c), rc,
+      __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(cst + r * LDC + c), rc,
                                              (int)off, 0, 17 /* sc0 sc1 */);
     }
     if (a.mark) tc_mark_ready_wt(a.h, a.rank, a.first_chunk + step / a.tiles_per_chunk);
