@@ -67,6 +67,31 @@ def test_deferred_marks_and_ctas_sweep():
             pair.close()
 
 
+def test_many_chunks():
+    # 275 one-tile chunks per rank, 1100 in all: more chunks than the
+    # completion check has threads, each chunk marked by its own CTA.
+    w = dict(P=4, rows=1100, cols=64, elem="u32", builder="tile_chunks", bm=4, bn=64,
+             tiles_per_chunk=1, rounds=2)
+    _run_all_rounds("many chunks", w)
+
+
+def test_large_pieces():
+    # Pieces of 1 MiB: a 1 MiB region per chunk goes to one wave whole.
+    w = dict(P=3, rows=512, cols=1024, elem="u32", builder="chunks", n=2, writers=4, rounds=2)
+    pair = Pair(w, piece_bytes=1 << 20)
+    try:
+        assert pair.plan.stats()["pieces"] == 6
+        for r in (1, 2):
+            log(f"large pieces round {r}")
+            pair.gpu_round_fill()
+            pair.oracle_round()
+            pair.compare(f"large pieces round {r}")
+            pair.plan.next_round()
+            pair.sim.next_round()
+    finally:
+        pair.close()
+
+
 def test_rank_that_sends_nothing_and_single_rank():
     w = dict(P=3, rows=20, cols=24, elem="u32", builder="chunks", n=2, writers=1, rounds=2)
     pair = Pair(w)
