@@ -319,22 +319,30 @@ enum { TC_FILL_U32 = 0, TC_FILL_BF16 = 1, TC_FILL_U8 = 2 };
 /* Mark modes: INKERNEL marks each chunk after writing it ([TP] Memory
  * ordering: mark_ready); NONE writes only (deferred marks: tc_mark_all). */
 enum { TC_MARK_INKERNEL = 0, TC_MARK_NONE = 1 };
+/* Fill modes.  A writer slot is one (rank, chunk, writer j): its CTA writes
+ * the j-th share of the chunk's bytes, then marks the chunk once.
+ *   PARALLEL: one CTA per writer slot, chunks of a rank in schedule order.
+ *   SERIAL:   one CTA per rank walks its chunks in order[] and, for each,
+ *             writes its writers' shares one after another, marking after
+ *             each.
+ *   WAVES:    a persistent grid of `ctas` CTAs takes the writer slots in
+ *             waves, every rank's chunk 0 first, then every rank's chunk 1,
+ *             ...; CTA i takes slots i, i + ctas, ...  Chunks complete a few
+ *             at a time, so the copy engine can deliver early chunks while
+ *             later ones are still produced ([TP] Model: a schedule lists
+ *             chunks in the order the producer completes them). */
+enum { TC_FILL_PARALLEL = 0, TC_FILL_SERIAL = 1, TC_FILL_WAVES = 2 };
 
 typedef struct tc_fill_desc {
   const tc_view* views;   /* host array of P views: rank p's part of the buffer */
   uint64_t seed;
   uint32_t kind;          /* TC_FILL_* ; elem_bytes of the views must match */
   uint32_t mark_mode;     /* TC_MARK_* */
-  /* serial = 0: one CTA per (rank, chunk, writer); CTA j of chunk c writes
-   *   the j-th share of c's bytes then marks once.  Chunks of a rank in
-   *   schedule order.
-   * serial = 1: one CTA per rank walks its chunks in order[] and, for each,
-   *   writes its writers' shares one after another, marking after each. */
-  uint32_t serial;
+  uint32_t mode;          /* TC_FILL_PARALLEL / TC_FILL_SERIAL / TC_FILL_WAVES */
   uint32_t rsvd;
-  const uint32_t* order;  /* device, [P][max_chunks] when serial; NULL = schedule order */
+  const uint32_t* order;  /* device, [P][max_chunks] when SERIAL; NULL = schedule order */
   uint32_t order_stride;  /* entries per rank in order[] */
-  uint32_t ctas_per_rank; /* serial mode: must be 1 */
+  uint32_t ctas;          /* WAVES: persistent grid size (0 = three CTAs per CU); else 0 */
 } tc_fill_desc;
 
 /* Hash-fill producer for every rank's chunks of `plan`, on `stream`.

@@ -120,10 +120,11 @@ class Pair:
         arr = np.stack([shuffled_order(self.seed, p, r, n) for p in range(self.P)])
         return arr, torch.from_numpy(arr.astype(np.int32)).cuda()
 
-    def gpu_round_fill(self, mark=True, serial=False, order=None, order_stride=0, timeout=10.0):
+    def gpu_round_fill(self, mark=True, serial=False, order=None, order_stride=0, timeout=10.0,
+                       **fill_kw):
         h = self.plan.start(self.stream)
         self.plan.fill(h, self.tv, self.seed, kind=self.w["elem"], mark=mark, serial=serial,
-                       order=order, order_stride=order_stride, stream=self.stream)
+                       order=order, order_stride=order_stride, stream=self.stream, **fill_kw)
         if not mark:
             self.plan.mark_all(h, stream=self.stream)
         self.plan.wait(timeout)

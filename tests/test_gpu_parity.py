@@ -67,6 +67,24 @@ def test_deferred_marks_and_ctas_sweep():
             pair.close()
 
 
+def test_waves_fill():
+    # A persistent producer grid completing every rank's chunk 0, then every
+    # rank's chunk 1, ...: grids smaller and larger than the slot count.
+    w = dict(workloads.SMALL["u32_chunks_ragged_p3"])
+    for ctas in (1, 4, 0):
+        pair = Pair(w)
+        try:
+            for r in (1, 2):
+                log(f"waves fill ctas={ctas} round {r}")
+                pair.gpu_round_fill(waves=True, ctas=ctas)
+                pair.oracle_round()
+                pair.compare(f"waves ctas={ctas} round {r}")
+                pair.plan.next_round()
+                pair.sim.next_round()
+        finally:
+            pair.close()
+
+
 def test_many_chunks():
     # 275 one-tile chunks per rank, 1100 in all: more chunks than the
     # completion check has threads, each chunk marked by its own CTA.

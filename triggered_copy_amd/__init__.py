@@ -16,6 +16,7 @@ import numpy as np
 
 from . import _lib
 from ._lib import (FILL_BF16, FILL_U8, FILL_U32, MARK_INKERNEL, MARK_NONE,  # noqa: F401
+                   FILL_PARALLEL, FILL_SERIAL, FILL_WAVES,
                    GATE_ROW_BYTES, TC_MAX_RANKS, Handle, View)
 
 __all__ = ["View", "Schedule", "whole", "chunks", "tile_chunks", "from_arrays", "order_grouped",
@@ -377,7 +378,11 @@ class TriggeredPlan:
 
     # -- synthetic producers / consumer on this plan
     def fill(self, handle, views, seed, kind="u32", mark=True, serial=False, order=None,
-             order_stride=0, stream=None):
+             order_stride=0, waves=False, ctas=0, stream=None):
+        """Hash-fill producer.  serial: one CTA per rank in order[];
+        waves: a persistent grid of `ctas` CTAs completing every rank's
+        chunk 0, then every rank's chunk 1, ...; otherwise one CTA per
+        writer."""
         kinds = {"u32": FILL_U32, "bf16": FILL_BF16, "u8": FILL_U8}
         va = (View * self.P)(*[_as_view(v, None) for v in views])
         d = _lib.FillDesc()
@@ -385,10 +390,10 @@ class TriggeredPlan:
         d.seed = seed
         d.kind = kinds[kind]
         d.mark_mode = MARK_INKERNEL if mark else MARK_NONE
-        d.serial = 1 if serial else 0
+        d.mode = FILL_SERIAL if serial else FILL_WAVES if waves else FILL_PARALLEL
         d.order = order.data_ptr() if order is not None else None
         d.order_stride = order_stride
-        d.ctas_per_rank = 1
+        d.ctas = ctas
         _check(lib().tc_produce_fill(self._p, C.byref(handle), C.byref(d), _stream_ptr(stream)))
 
     def mark_all(self, handle, stream=None):

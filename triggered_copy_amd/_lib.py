@@ -14,6 +14,7 @@ OK, EINVAL, EBOUNDS, EOVERLAP, ENOMEM, EHIP, ESTATE, ETIMEOUT, EEXTRA, EROUNDS, 
 STATE_NAMES = {0: "READY", 1: "STARTED", 2: "DONE", 3: "FAILED", 4: "CLOSED"}
 CHECK_OWN_ROWS = 1
 FILL_U32, FILL_BF16, FILL_U8 = 0, 1, 2
+FILL_PARALLEL, FILL_SERIAL, FILL_WAVES = 0, 1, 2
 MARK_INKERNEL, MARK_NONE = 0, 1
 
 u32, u64, vp = C.c_uint32, C.c_uint64, C.c_void_p
@@ -53,8 +54,8 @@ class Stats(C.Structure):
 
 class FillDesc(C.Structure):
     _fields_ = [("views", C.POINTER(View)), ("seed", u64), ("kind", u32), ("mark_mode", u32),
-                ("serial", u32), ("rsvd", u32), ("order", vp), ("order_stride", u32),
-                ("ctas_per_rank", u32)]
+                ("mode", u32), ("rsvd", u32), ("order", vp), ("order_stride", u32),
+                ("ctas", u32)]
 
 
 _SIGS = {

@@ -47,7 +47,7 @@ struct FillArgs {
   uint64_t seed_mix;
   uint32_t contiguous;                 // bit p: view p has row_stride == cols
   uint32_t kind, mark, elem;
-  uint32_t order_stride, G, pad0, pad1;
+  uint32_t order_stride, G, max_chunks, pad1;
 };
 
 __device__ inline uint64_t key_hash(const FillArgs& a, uint32_t p, uint64_t idx) {
@@ -169,6 +169,27 @@ __global__ __launch_bounds__(kFillThreads) void fill_serial_kernel(FillArgs a) {
   }
 }
 
+// Persistent grid: writer slots in waves (every rank's chunk 0 writers,
+// then every rank's chunk 1 writers, ...); CTA i takes slots i, i + ctas, ...
+// All loop bounds and indices are uniform over the CTA.
+__global__ __launch_bounds__(kFillThreads) void fill_waves_kernel(FillArgs a) {
+  uint64_t slot = 0;
+  for (uint32_t c = 0; c < a.max_chunks; ++c) {
+    for (uint32_t p = 0; p < a.h.nranks; ++p) {
+      if (c >= a.h.chunk_base[p + 1] - a.h.chunk_base[p]) continue;
+      const uint32_t g = a.h.chunk_base[p] + c;
+      const uint32_t w = a.chunks[g].writers;
+      // This CTA's slots among [slot, slot + w): j = first, first + grid, ...
+      const uint64_t first = (blockIdx.x + gridDim.x - slot % gridDim.x) % gridDim.x;
+      for (uint64_t j = first; j < w; j += gridDim.x) {
+        fill_share(a, g, (uint32_t)j);
+        if (a.mark == TC_MARK_INKERNEL) tc_mark_ready(a.h, p, c);
+      }
+      slot += w;
+    }
+  }
+}
+
 struct MarkArgs {
   tc_handle h;
   const uint64_t* wprefix;
@@ -259,14 +280,27 @@ int tc_produce_fill(tc_plan* P, const tc_handle* h, const tc_fill_desc* d, void*
   a.elem = elem;
   a.G = P->G;
   hipStream_t s = (hipStream_t)stream;
-  if (d->serial) {
-    if (d->ctas_per_rank > 1) return fail(TC_EINVAL, "fill: serial mode runs one CTA per rank");
+  if (d->mode != TC_FILL_WAVES && d->ctas) return fail(TC_EINVAL, "fill: ctas is for the waves mode");
+  if (d->mode != TC_FILL_SERIAL && d->order) return fail(TC_EINVAL, "fill: an order needs serial mode");
+  if (d->mode == TC_FILL_SERIAL) {
     hipLaunchKernelGGL(fill_serial_kernel, dim3(P->P), dim3(kFillThreads), 0, s, a);
-  } else {
-    if (d->order) return fail(TC_EINVAL, "fill: an order needs serial mode");
+  } else if (d->mode == TC_FILL_PARALLEL) {
     if (P->total_writers == 0) return TC_OK;
     if (P->total_writers > 0x7FFFFFFFull) return fail(TC_EINVAL, "fill: too many writers");
     hipLaunchKernelGGL(fill_parallel_kernel, dim3((uint32_t)P->total_writers), dim3(kFillThreads), 0, s, a);
+  } else if (d->mode == TC_FILL_WAVES) {
+    if (P->total_writers == 0) return TC_OK;
+    uint32_t ctas = d->ctas;
+    if (ctas == 0) {  // three 4-wave CTAs per CU: the hash fill needs them to keep the ALUs busy
+      int cus = 0;
+      TC_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, P->device));
+      ctas = 3u * (uint32_t)cus;
+    }
+    for (uint32_t p = 0; p < P->P; ++p)
+      a.max_chunks = std::max(a.max_chunks, P->chunk_base[p + 1] - P->chunk_base[p]);
+    hipLaunchKernelGGL(fill_waves_kernel, dim3(ctas), dim3(kFillThreads), 0, s, a);
+  } else {
+    return fail(TC_EINVAL, "fill: unknown mode");
   }
   TC_HIP(hipGetLastError());
   return TC_OK;
