@@ -230,6 +230,74 @@ def run_overlap(torch, tc, workloads, seed, reps=40, cu_mask=None, engine_ctas=0
                 delivered_gbs=P * (P - 1) * (B // P) / (statistics.median(rounds) * 1e-3) / 1e9)
 
 
+def run_consumer_overlap(torch, tc, workloads, seed, reps=20, N2=256):
+    """The 4 GEMM producers' round followed by each rank's in-kernel consumer
+    (Y_q = gathered rows of replica q [8000, 2000] x W [2000, 256]), three ways:
+    consumers launched after wait() returns ("sequential"); queued on the
+    producers' stream right behind them, waiting on the device for the
+    chunks still being copied ("chained"); and launched on a stream of their
+    own right after start(), before the producers ("early": their waiting
+    CTAs hold CUs the producers need)."""
+    from synth import gemm_operands
+    import numpy as np
+    w = workloads.FULL["gemm_tiles_p4"]
+    P, M, N, K = w["P"], w["rows"], w["cols"], w["K"]
+    views, rep, B = rank_setup(w, torch, tc)
+    ops = []
+    for p in range(P):
+        a, bt = gemm_operands(seed, p, 1, M, N, K)
+        ops.append((torch.from_numpy(a.view(np.int16)).cuda(), torch.from_numpy(bt.view(np.int16)).cuda()))
+    R = P * M
+    rng = np.random.default_rng(9)
+    wt = torch.from_numpy((rng.standard_normal((N2, N)).astype(np.float32).view(np.uint32) >> 16)
+                          .astype(np.uint16).view(np.int16)).cuda()
+    plan = tc.TriggeredPlan(rep, build_sched(w, views, tc))
+    start, pairs = plan.row_deps(tc.View(0, R, N, N, 2, 0), 128)
+    ds = torch.from_numpy(start.astype(np.int32)).cuda()
+    dp = torch.from_numpy(np.ascontiguousarray(pairs).astype(np.int32).reshape(-1)).cuda()
+    Y = [torch.zeros(R * N2, dtype=torch.int16, device="cuda") for _ in range(P)]
+    status = torch.zeros((P, len(start) - 1), dtype=torch.int32, device="cuda")
+    prod, cons = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def producers(h):
+        for p in range(P):
+            tc.gemm_bf16(ops[p][0], ops[p][1], rep[p][p * M * N * 2:], ldc=N, M=M, N=N,
+                         programs=w["programs"], group_m=w["group_m"], handle=h, rank=p,
+                         first_chunk=0, tiles_per_chunk=w["tiles_per_chunk"], stream=prod)
+
+    def consumers(h, stream, programs):
+        for q in range(P):
+            tc.gemm_consume_bf16(h, q, ds, dp, rep[q], wt, Y[q], M=R, N=N2, K=N, status=status[q],
+                                 programs=programs, stream=stream)
+
+    times = {"sequential": [], "chained": [], "early": []}
+    for i in range(reps + 2):
+        for mode in times:
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            h = plan.start(prod)
+            if mode == "early":      # half the CUs: the producers must find room
+                consumers(h, cons, 128)
+            producers(h)
+            if mode == "chained":
+                consumers(h, prod, 256)
+            plan.wait(30.0)
+            if mode == "sequential":
+                consumers(h, prod, 256)
+            torch.cuda.synchronize()
+            plan.next_round()
+            b = time.perf_counter()
+            if i >= 2:
+                times[mode].append((b - a) * 1e3)
+    bad = int((status != 0).sum().item())
+    plan.close()
+    flops = 2.0 * R * N2 * N * P
+    med = {k: statistics.median(v) for k, v in times.items()}
+    return dict(sequential_ms=med["sequential"], chained_ms=med["chained"], early_ms=med["early"],
+                chained_saved_pct=(1 - med["chained"] / med["sequential"]) * 100,
+                consumer_gflop=flops / 1e9, failed_waits=bad)
+
+
 def run_gemm_only(torch, tc, workloads, seed, reps):
     """The P GEMM producers back to back with no plan, `reps` times."""
     from synth import gemm_operands
@@ -394,6 +462,8 @@ def main():
         extras["gemm_overlap"] = run_overlap(torch, tc, workloads, BASE_SEED, cu_mask=mask,
                                              engine_ctas=args.overlap_engine_ctas)
         extras["gemm_overlap"]["engine_cus"] = args.overlap_cus or "all"
+        log("in-kernel consumers: after wait() vs waiting on the device")
+        extras["gemm_consumer"] = run_consumer_overlap(torch, tc, workloads, BASE_SEED)
         log("barrier: 8 ranks x 1000 generations")
         extras["barrier_p8"] = run_barrier(torch, tc, workloads)
         log("small rounds")

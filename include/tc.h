@@ -387,6 +387,36 @@ int tc_gemm_bf16(const void* A, const void* Bt, void* C, uint32_t M, uint32_t N,
 int tc_consume_copy(tc_plan* plan, const tc_handle* h, uint32_t dst, void* out_buf,
                     uint32_t max_polls, uint32_t* status, void* stream);
 
+/* Row dependencies of a consumer that reads the rows of `view` (relative to
+ * the plan's buffer, in every replica) in blocks of tile_rows: for row block
+ * b, the (src, chunk) pairs whose regions reach into rows [b * tile_rows,
+ * (b + 1) * tile_rows), conservatively (every row between a piece's first
+ * and last byte).  Host output, CSR: start[nblocks + 1] and pairs[2 * npairs]
+ * = (src, local chunk), a rank's own chunks included.  With start == pairs
+ * == NULL only *nblocks and *npairs are set (size query); otherwise
+ * pairs_cap counts pairs.  TC_EINVAL on a bad view or short arrays. */
+int tc_plan_row_deps(const tc_plan* plan, const tc_view* view, uint32_t tile_rows, uint32_t* start,
+                     uint32_t* pairs, uint32_t pairs_cap, uint32_t* nblocks, uint32_t* npairs);
+
+/* In-kernel consumer of the gathered rows ([TP] Memory ordering, consumer
+ * side; the step after the gather): Y[M,N] = X[M,K] * W, W given as Wt[N,K],
+ * bf16 in, fp32 accumulate, bf16 out, as tc_gemm_bf16.  X is rank dst's
+ * replica of the gathered view (device, row stride ldx elements).  Before a
+ * step reads its 128-row block b of X, the CTA waits (tc_wait: at most
+ * max_polls polls per chunk) for the pairs dep_pairs[2 d], d in
+ * [dep_start[b], dep_start[b + 1]) -- device copies of tc_plan_row_deps with
+ * tile_rows = 128.  status (device, one u32 per row block, may be NULL) gets
+ * 2 where a wait ran out of polls; the block is then computed from whatever
+ * the rows hold.  On one GPU the simulated ranks share the CUs: a consumer
+ * started before its producers must leave them room (programs at most half
+ * the CUs), or its waiting CTAs may hold every CU until their polls run out.
+ * TC_EINVAL as tc_gemm_bf16, or dst >= nranks, max_polls == 0. */
+int tc_gemm_consume_bf16(const tc_handle* h, uint32_t dst, const uint32_t* dep_start,
+                         const uint32_t* dep_pairs, uint32_t max_polls, uint32_t* status,
+                         const void* X, uint64_t ldx, const void* Wt, void* Y, uint32_t M,
+                         uint32_t N, uint32_t K, uint64_t ldy, uint32_t programs,
+                         uint32_t group_m, void* stream);
+
 /* ------------------------------------------------------------ barrier */
 
 /* Dedicated-row notify/wait barrier ([BAR] The idea; Walkthrough): one CTA

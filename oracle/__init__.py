@@ -25,9 +25,10 @@ Modules
 ``plan``      the step-by-step simulation of gates, in-order queues and rounds.
 ``barrier``   the notify/wait dedicated-row barrier, sequentially.
 ``gemm``      the fp32-accumulated reference for the GEMM producer.
+``consumer``  which chunks a consumer of the gathered rows waits for.
 
 Every function's pin (the independent fact that checks it) lives in
 ``tests/test_oracle_pins.py``.  Parts with no such pin say "parity unpinned".
 """
 
-from . import values, schedule, plan, barrier, gemm  # noqa: F401
+from . import values, schedule, plan, barrier, gemm, consumer  # noqa: F401

@@ -473,3 +473,62 @@ def test_gemm_reference_against_float64():
     bad = r64.copy()
     bad[3, 4] += 0.5 * np.sqrt(np.mean(r64 ** 2))
     assert not gemm.within_tolerance(bad, r64)[0]
+
+
+# ------------------------------------------------------------- consumer deps
+
+def _deps_brute(schedules, v, tile_rows):
+    """Every region byte enumerated: its view row and column decide its block."""
+    pitch, e = v.row_stride * v.elem_bytes, v.elem_bytes
+    nb = -(-v.rows // tile_rows)
+    deps = [set() for _ in range(nb)]
+    for p, s in enumerate(schedules):
+        if s is None:
+            continue
+        for c, ch in enumerate(s.chunks):
+            for off, rows, row_bytes, rpitch in ch.regions:
+                for i in range(rows):
+                    for byte in range(off + i * rpitch, off + i * rpitch + row_bytes):
+                        rel = byte - v.byte_offset
+                        if rel < 0 or rel >= v.rows * pitch or rel % pitch >= v.cols * e:
+                            continue
+                        deps[(rel // pitch) // tile_rows].add((p, c))
+    return [sorted(d) for d in deps]
+
+
+def test_consumer_row_deps_bruteforce():
+    from oracle import consumer as ocons
+    rng = np.random.default_rng(11)
+    for _ in range(40):
+        P = int(rng.integers(1, 4))
+        rows, cols = int(rng.integers(1, 10)), int(rng.integers(1, 9))
+        e = int(rng.choice([1, 2, 4]))
+        stride = cols + int(rng.integers(0, 3))
+        scheds = []
+        for p in range(P):
+            v = schedule.View(p * rows * stride * e, rows, cols, stride, e)
+            kind = int(rng.integers(0, 3))
+            if kind == 0:
+                scheds.append(schedule.whole(v, 1))
+            elif kind == 1:
+                scheds.append(schedule.chunks(v, int(rng.integers(1, rows + 1)), 1))
+            else:
+                scheds.append(schedule.tile_chunks(v, int(rng.integers(1, 4)), int(rng.integers(1, 4)),
+                                                 int(rng.integers(1, 4)), None))
+        gathered = schedule.View(0, P * rows, cols, stride, e)
+        tr = int(rng.integers(1, 7))
+        assert ocons.row_deps(scheds, gathered, tr) == _deps_brute(scheds, gathered, tr)
+
+
+def test_consumer_row_deps_rank_blocks():
+    # 128-row blocks over 4 ranks of 2000 rows each, one chunk per rank:
+    # block b depends on the ranks whose rows [2000 p, 2000 (p+1)) meet
+    # [128 b, 128 (b+1)) -- one rank, or two at a boundary.
+    from oracle import consumer as ocons
+    views = [schedule.View(p * 2000 * 64 * 2, 2000, 64, 64, 2) for p in range(4)]
+    scheds = [schedule.whole(v, 1) for v in views]
+    deps = ocons.row_deps(scheds, schedule.View(0, 8000, 64, 64, 2), 128)
+    assert len(deps) == 63
+    for b, d in enumerate(deps):
+        r0, r1 = 128 * b, min(8000, 128 * (b + 1)) - 1
+        assert d == [(p, 0) for p in range(r0 // 2000, r1 // 2000 + 1)]

@@ -20,7 +20,8 @@ from ._lib import (FILL_BF16, FILL_U8, FILL_U32, MARK_INKERNEL, MARK_NONE,  # no
                    GATE_ROW_BYTES, TC_MAX_RANKS, Handle, View)
 
 __all__ = ["View", "Schedule", "whole", "chunks", "tile_chunks", "from_arrays", "order_grouped",
-           "view_of", "TriggeredPlan", "gemm_bf16", "barrier", "TriggeredCopyError",
+           "view_of", "TriggeredPlan", "gemm_bf16", "gemm_consume_bf16", "barrier",
+           "TriggeredCopyError",
            "PlanTimeout", "ExtraMarksError", "StateError", "RoundLimitError"]
 
 
@@ -402,6 +403,21 @@ class TriggeredPlan:
     def mark(self, handle, rank, chunk, count=1, stream=None):
         _check(lib().tc_mark(self._p, C.byref(handle), rank, chunk, count, _stream_ptr(stream)))
 
+    def row_deps(self, view, tile_rows=128):
+        """(start [nblocks + 1], pairs [npairs, 2] = (src, chunk)) as uint32
+        numpy: the chunks each block of tile_rows rows of ``view`` waits for."""
+        v = _as_view(view, None)
+        nb, npairs = C.c_uint32(), C.c_uint32()
+        _check(lib().tc_plan_row_deps(self._p, C.byref(v), tile_rows, None, None, 0,
+                                      C.byref(nb), C.byref(npairs)))
+        start = np.zeros(nb.value + 1, dtype=np.uint32)
+        pairs = np.zeros((max(1, npairs.value), 2), dtype=np.uint32)
+        u32p = C.POINTER(C.c_uint32)
+        _check(lib().tc_plan_row_deps(self._p, C.byref(v), tile_rows,
+                                      start.ctypes.data_as(u32p), pairs.ctypes.data_as(u32p),
+                                      npairs.value, C.byref(nb), C.byref(npairs)))
+        return start, pairs[:npairs.value]
+
     def consume_copy(self, handle, dst, out, status, max_polls=1 << 20, stream=None):
         _check(lib().tc_consume_copy(self._p, C.byref(handle), dst, C.c_void_p(out.data_ptr()),
                                      max_polls, C.c_void_p(status.data_ptr()), _stream_ptr(stream)))
@@ -421,6 +437,18 @@ def gemm_bf16(A, Bt, C_out, *, ldc=None, programs=256, group_m=8, handle=None, r
     _check(lib().tc_gemm_bf16(C.c_void_p(A.data_ptr()), C.c_void_p(Bt.data_ptr()),
                               C.c_void_p(C_out.data_ptr()), M, N, K, ldc, programs, group_m, h,
                               rank, first_chunk, tiles_per_chunk, _stream_ptr(stream)))
+
+
+def gemm_consume_bf16(handle, dst, dep_start, dep_pairs, X, Wt, Y, *, M, N, K, ldx=None, ldy=None,
+                      status=None, max_polls=1 << 20, programs=128, group_m=8, stream=None):
+    """Y[M, N] = X[M, K] @ Wt[N, K].T where X is rank ``dst``'s replica of
+    gathered rows; each 128-row block first waits for its chunks
+    (``dep_start`` / ``dep_pairs``: device uint32 copies of
+    ``TriggeredPlan.row_deps(view, 128)``)."""
+    ptr = (lambda t: C.c_void_p(t.data_ptr()) if t is not None else None)
+    _check(lib().tc_gemm_consume_bf16(C.byref(handle), dst, ptr(dep_start), ptr(dep_pairs), max_polls,
+                                      ptr(status), ptr(X), ldx or K, ptr(Wt), ptr(Y), M, N, K, ldy or N,
+                                      programs, group_m, _stream_ptr(stream)))
 
 
 def barrier(W, P, first_gen, n_gen, status, *, x=None, y=None, snap=None, max_polls=1 << 22,

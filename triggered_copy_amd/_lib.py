@@ -87,6 +87,10 @@ _SIGS = {
     "tc_mark": [vp, C.POINTER(Handle), u32, u32, u32, vp],
     "tc_gemm_bf16": [vp, vp, vp, u32, u32, u32, u64, u32, u32, C.POINTER(Handle), u32, u32, u32, vp],
     "tc_consume_copy": [vp, C.POINTER(Handle), u32, vp, u32, vp, vp],
+    "tc_plan_row_deps": [vp, C.POINTER(View), u32, C.POINTER(u32), C.POINTER(u32), u32,
+                         C.POINTER(u32), C.POINTER(u32)],
+    "tc_gemm_consume_bf16": [C.POINTER(Handle), u32, vp, vp, u32, vp, vp, u64, vp, vp, u32, u32, u32,
+                             u64, u32, u32, vp],
     "tc_barrier_run": [vp, u32, u32, u32, vp, vp, vp, u32, vp, vp],
 }
 

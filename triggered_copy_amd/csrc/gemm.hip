@@ -11,6 +11,11 @@
 // operands stream along K), bf16 inputs, fp32 accumulation on the matrix
 // cores, bf16 output (round to nearest even).
 //
+// The same kernel is the in-kernel consumer of a gathered buffer ([TP]
+// Memory ordering, consumer side): A is a rank's replica of the gathered
+// rows, and before a step touches its 128-row block of A, the CTA waits
+// (tc_wait) for every chunk whose regions reach into those rows.
+//
 // gfx950 mapping: a 512-thread CTA computes a 128 x 128 tile with two groups
 // of 4 waves.  In each group the waves form a 2 x 2 grid of 64 x 64
 // sub-tiles, each 4 x 4 blocks of the 16x16x32 bf16 MFMA
@@ -50,11 +55,18 @@ struct GemmArgs {
   const uint16_t* A;
   const uint16_t* Bt;
   uint16_t* C;
-  uint64_t ldc;
+  uint64_t lda, ldc;
   uint32_t M, N, K;
   uint32_t tm, tn, group_m;
   uint32_t tiles;
   uint32_t mark, rank, first_chunk, tiles_per_chunk;
+  // Consumer mode (wait != 0): before a step, wait for the chunks listed for
+  // its 128-row block of A: pairs (src, chunk) dep_pairs[2 d], d in
+  // [dep_start[b], dep_start[b + 1]), as seen by rank dst.
+  uint32_t wait, dst, max_polls, pad;
+  const uint32_t* dep_start;
+  const uint32_t* dep_pairs;
+  uint32_t* status;  // per row block: 2 when a wait ran out of polls (may be NULL)
   tc_handle h;
 };
 
@@ -115,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
         const uint32_t r = v / kVecPerRow, kc = k0 + (v % kVecPerRow) * 8;
         const bool kin = kc < a.K;
         ra[s] = (m0 + r < a.M && kin)
-                    ? *reinterpret_cast<const u32x4*>(a.A + (uint64_t)(m0 + r) * a.K + kc)
+                    ? *reinterpret_cast<const u32x4*>(a.A + (uint64_t)(m0 + r) * a.lda + kc)
                     : u32x4{0, 0, 0, 0};
         rb[s] = (n0 + r < a.N && kin)
                     ? *reinterpret_cast<const u32x4*>(a.Bt + (uint64_t)(n0 + r) * a.K + kc)
@@ -135,6 +147,17 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
       }
     };
 
+    if (a.wait) {
+      // Whole-CTA waits with uniform bounds: every wave takes every wait.
+      const uint32_t b = m0 / BM;
+      const uint32_t d0 = tc_uniform(a.dep_start[b]), d1 = tc_uniform(a.dep_start[b + 1]);
+      bool ok = true;
+      for (uint32_t d = d0; d < d1; ++d)
+        if (!tc_wait(a.h, a.dst, tc_uniform(a.dep_pairs[2 * d]), tc_uniform(a.dep_pairs[2 * d + 1]),
+                     a.max_polls))
+          ok = false;
+      if (!ok && a.status && tc_is_cta_leader()) a.status[b] = 2u;
+    }
     __syncthreads();  // the previous tile's partial sums and C staging are no longer read
     if (grp < nk) {
       fetch(grp);
@@ -226,25 +249,28 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
 
 }  // namespace
 
-extern "C" int tc_gemm_bf16(const void* A, const void* Bt, void* C, uint32_t M, uint32_t N,
-                            uint32_t K, uint64_t ldc, uint32_t programs, uint32_t group_m,
-                            const tc_handle* h, uint32_t rank, uint32_t first_chunk,
-                            uint32_t tiles_per_chunk, void* stream) {
+static int check_gemm_shape(const void* A, const void* Bt, const void* C, uint32_t M, uint32_t N,
+                            uint32_t K, uint64_t lda, uint64_t ldc, uint32_t programs,
+                            uint32_t group_m) {
   if (!A || !Bt || !C) return fail(TC_EINVAL, "gemm: NULL operand");
   if (M == 0 || N == 0 || K == 0 || programs == 0 || group_m == 0)
     return fail(TC_EINVAL, "gemm: zero size");
-  if (K % 8 || N % 8 || ldc % 8 || ldc < N)
-    return fail(TC_EINVAL, "gemm: K, N and ldc must be multiples of 8 (16-byte rows), ldc >= N");
+  if (K % 8 || N % 8 || ldc % 8 || ldc < N || lda % 8 || lda < K)
+    return fail(TC_EINVAL, "gemm: K, N, lda and ldc must be multiples of 8 (16-byte rows), "
+                           "lda >= K, ldc >= N");
   if ((uint64_t)BM * ldc * 2 >= (1ull << 31))
     return fail(TC_EINVAL, "gemm: a 128-row tile of C must span less than 2 GiB (ldc < 2^23)");
   if (((uintptr_t)A | (uintptr_t)Bt | (uintptr_t)C) & 15)
     return fail(TC_EINVAL, "gemm: operands must be 16-byte aligned");
-  if (h && (tiles_per_chunk == 0 || rank >= h->nranks))
-    return fail(TC_EINVAL, "gemm: bad rank or tiles_per_chunk");
-  GemmArgs a{};
+  return TC_OK;
+}
+
+static void fill_shape(GemmArgs& a, const void* A, const void* Bt, void* C, uint32_t M, uint32_t N,
+                       uint32_t K, uint64_t lda, uint64_t ldc, uint32_t group_m) {
   a.A = (const uint16_t*)A;
   a.Bt = (const uint16_t*)Bt;
   a.C = (uint16_t*)C;
+  a.lda = lda;
   a.ldc = ldc;
   a.M = M;
   a.N = N;
@@ -253,6 +279,24 @@ extern "C" int tc_gemm_bf16(const void* A, const void* Bt, void* C, uint32_t M, 
   a.tn = (N + BN - 1) / BN;
   a.group_m = group_m;
   a.tiles = a.tm * a.tn;
+}
+
+static int launch(const GemmArgs& a, uint32_t programs, void* stream) {
+  hipLaunchKernelGGL(gemm_kernel, dim3(programs), dim3(kThreads), 0, (hipStream_t)stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return tc::hip_fail(e, "gemm launch");
+  return TC_OK;
+}
+
+extern "C" int tc_gemm_bf16(const void* A, const void* Bt, void* C, uint32_t M, uint32_t N,
+                            uint32_t K, uint64_t ldc, uint32_t programs, uint32_t group_m,
+                            const tc_handle* h, uint32_t rank, uint32_t first_chunk,
+                            uint32_t tiles_per_chunk, void* stream) {
+  if (int rc = check_gemm_shape(A, Bt, C, M, N, K, K, ldc, programs, group_m)) return rc;
+  if (h && (tiles_per_chunk == 0 || rank >= h->nranks))
+    return fail(TC_EINVAL, "gemm: bad rank or tiles_per_chunk");
+  GemmArgs a{};
+  fill_shape(a, A, Bt, C, M, N, K, K, ldc, group_m);
   if (h) {
     a.mark = 1;
     a.h = *h;
@@ -263,8 +307,26 @@ extern "C" int tc_gemm_bf16(const void* A, const void* Bt, void* C, uint32_t M, 
     if (first_chunk + (a.tiles - 1) / tiles_per_chunk >= nchunks)
       return fail(TC_EINVAL, "gemm: the tiles map past the rank's chunks");
   }
-  hipLaunchKernelGGL(gemm_kernel, dim3(programs), dim3(kThreads), 0, (hipStream_t)stream, a);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return tc::hip_fail(e, "gemm launch");
-  return TC_OK;
+  return launch(a, programs, stream);
+}
+
+extern "C" int tc_gemm_consume_bf16(const tc_handle* h, uint32_t dst, const uint32_t* dep_start,
+                                    const uint32_t* dep_pairs, uint32_t max_polls,
+                                    uint32_t* status, const void* X, uint64_t ldx, const void* Wt,
+                                    void* Y, uint32_t M, uint32_t N, uint32_t K, uint64_t ldy,
+                                    uint32_t programs, uint32_t group_m, void* stream) {
+  if (!h || !dep_start || !dep_pairs) return fail(TC_EINVAL, "consume gemm: NULL argument");
+  if (dst >= h->nranks) return fail(TC_EINVAL, "consume gemm: dst out of range");
+  if (max_polls == 0) return fail(TC_EINVAL, "consume gemm: max_polls is 0");
+  if (int rc = check_gemm_shape(X, Wt, Y, M, N, K, ldx, ldy, programs, group_m)) return rc;
+  GemmArgs a{};
+  fill_shape(a, X, Wt, Y, M, N, K, ldx, ldy, group_m);
+  a.h = *h;
+  a.wait = 1;
+  a.dst = dst;
+  a.max_polls = max_polls;
+  a.dep_start = dep_start;
+  a.dep_pairs = dep_pairs;
+  a.status = status;
+  return launch(a, programs, stream);
 }

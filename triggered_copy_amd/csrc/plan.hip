@@ -945,6 +945,56 @@ int tc_plan_read_gates(tc_plan* P, void* host, uint64_t bytes) {
   return TC_OK;
 }
 
+int tc_plan_row_deps(const tc_plan* P, const tc_view* view, uint32_t tile_rows, uint32_t* start,
+                     uint32_t* pairs, uint32_t pairs_cap, uint32_t* nblocks, uint32_t* npairs) {
+  if (!P || !view || !nblocks || !npairs) return fail(TC_EINVAL, "row_deps: NULL argument");
+  if (tile_rows == 0 || view->rows == 0 || view->cols == 0 || view->elem_bytes == 0 ||
+      view->row_stride < view->cols)
+    return fail(TC_EINVAL, "row_deps: bad view or tile_rows");
+  const uint64_t pitch = view->row_stride * view->elem_bytes;
+  const uint64_t base = view->byte_offset, end = base + view->rows * pitch;
+  const uint64_t nb = (view->rows + tile_rows - 1) / tile_rows;
+  if (nb >= (1ull << 31)) return fail(TC_EINVAL, "row_deps: too many row blocks");
+  // Row blocks each chunk's pieces reach into (conservatively: every row
+  // between a piece's first and last byte).
+  std::vector<std::vector<uint32_t>> blk(nb);
+  for (uint32_t g = 0; g < P->G; ++g) {
+    const ChunkD& cd = P->chunks[g];
+    for (uint32_t k = 0; k < cd.npieces; ++k) {
+      const PieceD& pc = P->pieces[cd.first_piece + k];
+      const uint64_t a = pc.off, b = pc.off + (pc.rows - 1) * pc.pitch + pc.row_bytes;  // [a, b)
+      if (b <= base || a >= end) continue;
+      const uint64_t r0 = (std::max(a, base) - base) / pitch;
+      const uint64_t r1 = (std::min(b, end) - 1 - base) / pitch;
+      for (uint64_t t = r0 / tile_rows; t <= r1 / tile_rows; ++t)
+        if (blk[t].empty() || blk[t].back() != g) blk[t].push_back(g);
+    }
+  }
+  uint64_t total = 0;
+  for (auto& v : blk) {
+    std::sort(v.begin(), v.end());
+    v.erase(std::unique(v.begin(), v.end()), v.end());
+    total += v.size();
+  }
+  if (total >= (1ull << 31)) return fail(TC_EINVAL, "row_deps: too many dependencies");
+  *nblocks = (uint32_t)nb;
+  *npairs = (uint32_t)total;
+  if (!start && !pairs) return TC_OK;  // size query
+  if (!start || !pairs || pairs_cap < total)
+    return fail(TC_EINVAL, "row_deps: start needs nblocks + 1 entries and pairs 2 * npairs");
+  uint32_t at = 0;
+  for (uint64_t t = 0; t < nb; ++t) {
+    start[t] = at;
+    for (uint32_t g : blk[t]) {
+      pairs[2 * at] = P->chunks[g].rank;
+      pairs[2 * at + 1] = P->chunks[g].local;
+      ++at;
+    }
+  }
+  start[nb] = at;
+  return TC_OK;
+}
+
 int tc_plan_read_cursors(tc_plan* P, uint32_t* host) {
   if (!P || !host) return fail(TC_EINVAL, "read_cursors: NULL argument");
   const uint8_t* blk = P->ws + P->L.round_blk[P->round & 1u];
