@@ -65,7 +65,8 @@ enum tc_plan_state_t {
   TC_STATE_STARTED = 1, /* start() returned; marks and copies may be in flight */
   TC_STATE_DONE = 2,    /* wait() found every chunk delivered everywhere */
   TC_STATE_FAILED = 3,  /* extra marks or corrupt gates: only close() is allowed */
-  TC_STATE_CLOSED = 4
+  TC_STATE_CLOSED = 4,
+  TC_STATE_CLOSING = 5  /* close() found its copies queued behind another plan's */
 };
 
 /* Plan-creation flags. */
@@ -269,10 +270,20 @@ int tc_plan_wait(tc_plan* plan, uint64_t timeout_us);
  * round + 1.  TC_ESTATE unless DONE; TC_EROUNDS at round 2^32 - 1. */
 int tc_plan_next_round(tc_plan* plan);
 
-/* Stops the copy engine if it runs, waits for it, and frees the plan's
- * streams, events and host words ([TP] Model: close / leaving the with
- * block).  Safe in any state; the caller's buffers are not touched. */
-int tc_plan_close(tc_plan* plan);
+/* Closes the plan ([TP] Model: close / leaving the with block; The kernel
+ * author's contract: closing mid-round).  Safe in any state.  In the middle
+ * of a round every gate of the plan is forced open, so the copy engine sends
+ * each rank's chunks as they stand (after a timeout it is run again for
+ * that); then its streams, events and host words are freed.  The caller's
+ * buffers keep what was delivered.  Plans with the same CU mask share one
+ * engine stream, so their rounds run in start() order; a plan whose engine
+ * is still queued behind another plan's waiting engine cannot finish first.
+ * With closing != NULL such a close() returns TC_OK with *closing = 1 and the
+ * plan CLOSING (still valid): closing the earlier plan lets it finish, and a
+ * later tc_plan_close frees it.  Otherwise (*closing = 0) the plan is freed.
+ * With closing == NULL the call waits for the engine.  TC_ETIMEOUT when the
+ * engine does not stop within 10 s (the plan is then leaked, not freed). */
+int tc_plan_close(tc_plan* plan, int* closing);
 
 int tc_plan_state(const tc_plan* plan, int* state, uint32_t* round);
 

@@ -85,6 +85,77 @@ def test_waves_fill():
             pair.close()
 
 
+def _expected_replicas(pair, r):
+    """Every replica after round r delivered in full (oracle)."""
+    pair.oracle_round()
+    return [rep.copy() for rep in pair.sim.rep]
+
+
+def test_close_mid_round_sends_chunks_as_they_stand():
+    w = dict(workloads.SMALL["u32_chunks_ragged_p3"])
+    pair = Pair(w)
+    try:
+        h = pair.plan.start(pair.stream)
+        # data written, only rank 0's chunks marked: the others' gates stay shut
+        pair.plan.fill(h, pair.tv, pair.seed, kind="u32", mark=False, stream=pair.stream)
+        for c in range(5):
+            pair.plan.mark(h, 0, c, 2, stream=pair.stream)
+        pair.stream.synchronize()
+        assert pair.plan.close() == "CLOSED"
+        want = _expected_replicas(pair, 1)
+        host = pair.rep.cpu().numpy()
+        for q in range(pair.P):
+            assert np.array_equal(host[q], want[q]), f"replica {q} after close"
+    finally:
+        pair.close()
+
+
+def test_close_after_timeout_sends_chunks_as_they_stand():
+    w = dict(workloads.SMALL["u32_whole_p5"])
+    pair = Pair(w)
+    try:
+        h = pair.plan.start(pair.stream)
+        pair.plan.fill(h, pair.tv, pair.seed, kind="u32", mark=False, stream=pair.stream)
+        with pytest.raises(tc.PlanTimeout):
+            pair.plan.wait(0.2)            # the engine is stopped
+        pair.stream.synchronize()
+        assert pair.plan.close() == "CLOSED"
+        want = _expected_replicas(pair, 1)
+        host = pair.rep.cpu().numpy()
+        for q in range(pair.P):
+            assert np.array_equal(host[q], want[q]), f"replica {q} after close"
+    finally:
+        pair.close()
+
+
+def test_plan_queued_behind_another_is_closing():
+    # Two plans over the same buffers (row blocks, and the whole block) share
+    # the engine stream: B's round is queued behind A's, whose gates stay
+    # shut.  B's close() returns CLOSING; closing A sends A's chunks as they
+    # stand and lets B's engine run; B's second close() frees it.
+    w = dict(P=3, rows=24, cols=40, elem="u32", builder="chunks", n=3, writers=1, rounds=1)
+    pair = Pair(w)
+    b = tc.TriggeredPlan(pair.rep, [tc.whole(v, 1) for v in pair.tv], backstop_s=20.0)
+    try:
+        ha = pair.plan.start(pair.stream)
+        hb = b.start(pair.stream)
+        pair.plan.fill(ha, pair.tv, pair.seed, kind="u32", mark=False, stream=pair.stream)
+        pair.stream.synchronize()
+        assert b.close() == "CLOSING"
+        assert b.state == "CLOSING"
+        assert pair.plan.close() == "CLOSED"
+        # B's engine starts once A's has left the stream
+        assert wait_until(lambda: b.close() == "CLOSED", 5.0)
+        want = _expected_replicas(pair, 1)
+        host = pair.rep.cpu().numpy()
+        for q in range(pair.P):
+            assert np.array_equal(host[q], want[q]), f"replica {q} after closing both"
+        del hb
+    finally:
+        b.close()
+        pair.close()
+
+
 def test_many_chunks():
     # 275 one-tile chunks per rank, 1100 in all: more chunks than the
     # completion check has threads, each chunk marked by its own CTA.

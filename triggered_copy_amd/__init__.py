@@ -293,10 +293,20 @@ class TriggeredPlan:
         return False
 
     def close(self):
-        if getattr(self, "_p", None) is not None and self._p.value:
-            rc = lib().tc_plan_close(self._p)
+        """Closes the plan; mid-round, every chunk is sent as it stands.
+        Returns "CLOSED", or "CLOSING" when this plan's copies are queued
+        behind another plan's waiting ones: close that plan, then call
+        close() here again."""
+        if getattr(self, "_p", None) is None or not self._p.value:
+            return "CLOSED"
+        closing = C.c_int(0)
+        rc = lib().tc_plan_close(self._p, C.byref(closing))
+        if rc == _lib.OK and closing.value:
+            return "CLOSING"
+        if rc == _lib.OK:
             self._p = C.c_void_p(0)
-            _check(rc)
+        _check(rc)
+        return "CLOSED"
 
     def __del__(self):
         try:

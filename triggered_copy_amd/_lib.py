@@ -11,7 +11,7 @@ GATE_ROW_BYTES = 64
 
 OK, EINVAL, EBOUNDS, EOVERLAP, ENOMEM, EHIP, ESTATE, ETIMEOUT, EEXTRA, EROUNDS, ENODEV, ECORRUPT = \
     0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11
-STATE_NAMES = {0: "READY", 1: "STARTED", 2: "DONE", 3: "FAILED", 4: "CLOSED"}
+STATE_NAMES = {0: "READY", 1: "STARTED", 2: "DONE", 3: "FAILED", 4: "CLOSED", 5: "CLOSING"}
 CHECK_OWN_ROWS = 1
 FILL_U32, FILL_BF16, FILL_U8 = 0, 1, 2
 FILL_PARALLEL, FILL_SERIAL, FILL_WAVES = 0, 1, 2
@@ -74,7 +74,7 @@ _SIGS = {
     "tc_plan_wait": [vp, u64],
     "tc_plan_handle": [vp, C.POINTER(Handle)],
     "tc_plan_next_round": [vp],
-    "tc_plan_close": [vp],
+    "tc_plan_close": [vp, C.POINTER(C.c_int)],
     "tc_plan_state": [vp, C.POINTER(C.c_int), C.POINTER(u32)],
     "tc_plan_problems": [vp, C.POINTER(u32), u32, C.POINTER(u32)],
     "tc_plan_read_gates": [vp, vp, u64],

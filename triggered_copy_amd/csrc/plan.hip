@@ -128,6 +128,7 @@ struct EngineArgs {
   uint32_t* cur;          // this round: cursor[p*P + q]
   uint32_t* zero_round;   // the other round block, cleared for the next round
   const uint32_t* abort_word;  // pinned host word: launches <= it must stop
+  const uint32_t* force;       // device word: nonzero once close() sends chunks as they stand
   uint32_t* status;
   uint32_t piece_base[TC_MAX_RANKS + 1];
   uint32_t round;
@@ -371,9 +372,12 @@ __global__ __launch_bounds__(kEngineThreads) void engine_kernel(EngineArgs a) {
       const PieceD pc = a.pieces[a.piece_base[p] + t];
       const uint32_t g = tc_uniform(pc.chunk);
       if (g != acquired) {
-        // The gate of round r is open once the chunk's marks reach r * writers.
+        // The gate of round r is open once the chunk's marks reach r * writers
+        // (or once close() forces every gate of the plan open).
         const uint64_t want = (uint64_t)a.round * tc_uniform(a.chunks[g].writers);
-        if (!poll_until(a, t0, gate_mode, [&] { return mark_count(a, g) >= want; })) return;
+        if (!poll_until(a, t0, gate_mode,
+                        [&] { return mark_count(a, g) >= want || wave_load_sys(a.force) != 0; }))
+          return;
         // The wave holding a chunk's first piece records when it saw the gate open.
         if (a.piece_base[p] + t == a.chunks[g].first_piece) wave_max32(&a.stats[0], ~(uint32_t)now_ticks());
         acquired = g;
@@ -532,6 +536,7 @@ static int launch_engine(tc_plan* P) {
   a.zero_round_words = (uint32_t)(L.round_bytes / 4);
   a.abort_word = P->abort_dev;
   a.status = reinterpret_cast<uint32_t*>(P->ws + L.status);
+  a.force = reinterpret_cast<const uint32_t*>(P->ws + L.status + kForceOffset);
   for (uint32_t p = 0; p <= P->P; ++p) a.piece_base[p] = P->piece_base[p];
   a.round = P->round;
   a.nranks = P->P;
@@ -881,21 +886,48 @@ int tc_plan_next_round(tc_plan* P) {
   return TC_OK;
 }
 
-int tc_plan_close(tc_plan* P) {
+int tc_plan_close(tc_plan* P, int* closing) {
+  if (closing) *closing = 0;
   if (!P) return TC_OK;
-  int rc = TC_OK;
-  if (P->launch_id) {
-    __atomic_store_n(P->abort_host, P->launch_id, __ATOMIC_SEQ_CST);
-    hipError_t err = hipSuccess;
-    const auto drain = std::chrono::steady_clock::now() + std::chrono::seconds(10);
-    // The engine stream may be shared with other plans: wait for this plan's
-    // own work only.
-    if (event_done_by(P->ev_engine_done, drain, &err) != 1 ||
-        (P->check_seq && event_done_by(P->ev_check_done, drain, &err) != 1))
-      rc = fail(TC_ETIMEOUT, "close: copy engine did not stop within 10 s");
+  const auto deadline = [](int s) { return std::chrono::steady_clock::now() + std::chrono::seconds(s); };
+  hipError_t err = hipSuccess;
+  const bool mid_round = P->state == TC_STATE_STARTED || P->state == TC_STATE_CLOSING;
+  if (mid_round && !P->forced) {
+    // Send every chunk as it stands ([TP] The kernel author's contract:
+    // closing mid-round): force every gate open, and run the engine again if
+    // a timeout stopped it.
+    const uint32_t one = 1;
+    TC_HIP(hipMemcpyAsync(P->ws + P->L.status + kForceOffset, &one, 4, hipMemcpyHostToDevice,
+                          P->aux_stream));
+    TC_HIP(hipStreamSynchronize(P->aux_stream));
+    P->forced = true;
+    if (P->need_relaunch) {
+      if (int rc = launch_engine(P)) return rc;
+      P->need_relaunch = false;
+    }
   }
-  if (rc == TC_OK) destroy(P);  // on failure leak rather than free memory a kernel may touch
-  return rc;
+  if (P->launch_id) {
+    // The engine stream may be shared with other plans: this plan's launch
+    // may still be queued behind another plan's engine, which waits for that
+    // plan's gates.  Then the plan stays CLOSING; closing the earlier plan
+    // lets this one finish, and a later close() frees it.
+    if (closing && hipEventQuery(P->ev_engine_start) == hipErrorNotReady) {
+      P->state = TC_STATE_CLOSING;
+      *closing = 1;
+      return TC_OK;
+    }
+    int done = event_done_by(P->ev_engine_done, deadline(10), &err);
+    if (done != 1) {  // the forced engine did not finish: stop it
+      __atomic_store_n(P->abort_host, P->launch_id, __ATOMIC_SEQ_CST);
+      done = event_done_by(P->ev_engine_done, deadline(10), &err);
+    }
+    if (done != 1 || (P->check_seq && event_done_by(P->ev_check_done, deadline(10), &err) != 1)) {
+      // Leak rather than free memory a kernel may still touch.
+      return fail(TC_ETIMEOUT, "close: copy engine did not stop within 10 s");
+    }
+  }
+  destroy(P);
+  return TC_OK;
 }
 
 int tc_plan_state(const tc_plan* P, int* state, uint32_t* round) {

@@ -14,6 +14,8 @@ namespace tc {
 constexpr uint32_t kTicketStride = 32;  // u32 words between hot counters: one 128-byte line each
 constexpr uint32_t kStatsWords = 2;     // u64 words of per-launch timestamps
 
+constexpr uint64_t kForceOffset = 128;  // byte offset of the force word in the status block
+
 constexpr uint32_t kStatusAborted = 1;  // engine stopped by the host's abort word
 constexpr uint32_t kStatusExpired = 2;  // engine stopped by its wall-clock backstop
 
@@ -76,6 +78,7 @@ struct tc_plan {
   uint32_t cur_launch_block = 0;
   uint32_t launches_this_round = 0;
   bool need_relaunch = false;
+  bool forced = false;       // close() has forced every gate open
   float last_engine_ms = 0.f;
   bool engine_ms_pending = false;  // last_engine_ms not yet read from the events
   std::vector<uint32_t> problems;  // (rank, chunk) pairs
