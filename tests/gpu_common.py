@@ -81,6 +81,18 @@ def oracle_produce(rep, v, kind, seed, p, r):
             rep[a:a + v.cols * e] = vals[i]
 
 
+def oracle_produce_regions(rep, v, sched, kind, seed, p, r):
+    """As oracle_produce, but only the bytes of ``sched``'s regions: what a
+    producer that writes exactly its scheduled regions leaves."""
+    tmp = rep.copy()
+    oracle_produce(tmp, v, kind, seed, p, r)
+    for ch in sched.chunks:
+        for off, rows, rb, pitch in ch.regions:
+            for i in range(rows):
+                a = off + i * pitch
+                rep[a:a + rb] = tmp[a:a + rb]
+
+
 def gate_array(sim):
     return sim.gate_bytes()
 

@@ -156,6 +156,87 @@ def test_plan_queued_behind_another_is_closing():
         pair.close()
 
 
+def _swap_in(pair, tsched, osched_list, **plan_kw):
+    """Replace the Pair's plan and oracle with other schedules on the same buffers."""
+    pair.plan.close()
+    pair.plan = tc.TriggeredPlan(pair.rep, tsched, backstop_s=20.0, **plan_kw)
+    pair.ts, pair.os = tsched, osched_list
+    pair.sim = oplan.PlanSim(pair.sim.rep, osched_list)
+
+
+def _rounds(pair, n, what):
+    for r in range(1, n + 1):
+        log(f"{what} round {r}")
+        h = pair.plan.start(pair.stream)
+        pair.plan.fill(h, pair.tv, pair.seed, kind=pair.w["elem"], stream=pair.stream)
+        pair.plan.wait(10.0)
+
+        def produce(p, rr):
+            if pair.os[p] is not None:
+                from tests.gpu_common import oracle_produce_regions
+                oracle_produce_regions(pair.sim.rep[p], pair.ov[p], pair.os[p], pair.w["elem"],
+                                       pair.seed, p, rr)
+        oplan.run_round(pair.sim, produce)
+        pair.compare(f"{what} round {r}")
+        pair.plan.next_round()
+        pair.sim.next_round()
+
+
+def test_broadcast_from_one_rank():
+    # Only rank 0 sends (the others pass empty schedules): a broadcast.
+    w = dict(P=4, rows=33, cols=50, elem="u32", builder="chunks", n=3, writers=2, rounds=2)
+    pair = Pair(w)
+    try:
+        _swap_in(pair, [pair.ts[0], None, None, None], [pair.os[0], None, None, None])
+        _rounds(pair, 2, "broadcast")
+    finally:
+        pair.close()
+
+
+def test_hand_built_schedules():
+    # Regions that cut tiles and regions that span several: part of a tile,
+    # three tiles side by side as one 2-D window, a linear range across row
+    # ends, all in one chunk table with 1-3 writers per chunk.
+    from oracle import schedule as osched
+    w = dict(P=3, rows=24, cols=40, elem="u8", builder="whole", writers=1, rounds=2)
+    pair = Pair(w)
+    try:
+        rows, cols = w["rows"], w["cols"]
+        ts, os_ = [], []
+        for p in range(3):
+            base = p * rows * cols
+            regions = [
+                (base + 2 * cols + 3, 5, 7, cols),          # 5 x 7 piece of a tile
+                (base + 8 * cols, 4, 36, cols),             # 3 tiles of 12 columns side by side
+                (base + 13 * cols + 30, 1, 25, 25),         # linear across a row end
+                (base + 20 * cols, 4, cols, cols),          # whole rows: linear after normalising
+            ]
+            chunks = [(0, 1, 1), (1, 2, 3), (3, 1, 2)]
+            ts.append(tc.from_arrays(chunks, regions))
+            os_.append(osched.from_tables(chunks, regions))
+        _swap_in(pair, ts, os_)
+        _rounds(pair, 2, "hand-built")
+    finally:
+        pair.close()
+
+
+def test_prepare_all_gather_default_whole():
+    w = dict(P=3, rows=16, cols=64, elem="u32", builder="whole", writers=4, rounds=2)
+    pair = Pair(w)
+    try:
+        pair.plan.close()
+        pair.plan, views = tc.prepare_all_gather(pair.rep, w["rows"], w["cols"], 4, writers=4,
+                                                 backstop_s=20.0)
+        assert [v.byte_offset for v in views] == [t.byte_offset for t in pair.tv]
+        _rounds(pair, 2, "prepare_all_gather")
+        # a schedule reaching into the next rank's rows is refused
+        bad = [tc.whole(tc.View(0, 17, 64, 64, 4, 0), 1), None, None]
+        with pytest.raises(tc.BoundsError):
+            tc.prepare_all_gather(pair.rep, w["rows"], w["cols"], 4, schedules=bad)
+    finally:
+        pair.close()
+
+
 def test_many_chunks():
     # 275 one-tile chunks per rank, 1100 in all: more chunks than the
     # completion check has threads, each chunk marked by its own CTA.

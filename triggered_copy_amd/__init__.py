@@ -20,7 +20,8 @@ from ._lib import (FILL_BF16, FILL_U8, FILL_U32, MARK_INKERNEL, MARK_NONE,  # no
                    GATE_ROW_BYTES, TC_MAX_RANKS, Handle, View)
 
 __all__ = ["View", "Schedule", "whole", "chunks", "tile_chunks", "from_arrays", "order_grouped",
-           "view_of", "TriggeredPlan", "gemm_bf16", "gemm_consume_bf16", "barrier",
+           "view_of", "TriggeredPlan", "prepare_all_gather", "gemm_bf16", "gemm_consume_bf16",
+           "barrier",
            "TriggeredCopyError",
            "PlanTimeout", "ExtraMarksError", "StateError", "RoundLimitError"]
 
@@ -434,6 +435,20 @@ class TriggeredPlan:
 
 
 # -------------------------------------------------------------- producers
+
+def prepare_all_gather(replicas, rows, cols, elem_bytes, schedules=None, writers=1, **plan_kw):
+    """The in-place all-gather plan: rank p owns rows [p * rows, (p + 1) * rows)
+    of a [P * rows, cols] buffer (one replica per rank), sends them as one
+    whole() chunk with ``writers`` marks unless ``schedules`` are given, and
+    the plan checks that no rank's schedule leaves its own rows.  Returns
+    (plan, views)."""
+    P = replicas.shape[0] if hasattr(replicas, "shape") and len(replicas.shape) == 2 else len(replicas)
+    own = rows * cols * elem_bytes
+    views = [View(p * own, rows, cols, cols, elem_bytes, 0) for p in range(P)]
+    if schedules is None:
+        schedules = [whole(v, writers) for v in views]
+    return TriggeredPlan(replicas, schedules, own_rows_bytes=own, **plan_kw), views
+
 
 def gemm_bf16(A, Bt, C_out, *, ldc=None, programs=256, group_m=8, handle=None, rank=0,
               first_chunk=0, tiles_per_chunk=256, M=None, N=None, stream=None):
