@@ -911,7 +911,8 @@ int tc_plan_close(tc_plan* P, int* closing) {
     // may still be queued behind another plan's engine, which waits for that
     // plan's gates.  Then the plan stays CLOSING; closing the earlier plan
     // lets this one finish, and a later close() frees it.
-    if (closing && hipEventQuery(P->ev_engine_start) == hipErrorNotReady) {
+    // (A launch just submitted needs a moment to start: give it one second.)
+    if (closing && event_done_by(P->ev_engine_start, deadline(1), &err) == 0) {
       P->state = TC_STATE_CLOSING;
       *closing = 1;
       return TC_OK;
