@@ -298,6 +298,34 @@ def run_consumer_overlap(torch, tc, workloads, seed, reps=20, N2=256):
                 consumer_gflop=flops / 1e9, failed_waits=bad)
 
 
+def run_placement_trials(torch, tc, workloads, seed, trials, rounds=6):
+    """Copy-engine bandwidth on the headline workload for `trials` fresh
+    allocations of the replicas (each freed before the next): where the
+    driver places the replicas' pages in HBM changes the engine's rate."""
+    w = workloads.FULL["u32_chunks_1p5g_p4"]
+    P = w["P"]
+    out = []
+    for _ in range(trials):
+        views, rep, B = rank_setup(w, torch, tc)
+        plan = tc.TriggeredPlan(rep, build_sched(w, views, tc))
+        prod = torch.cuda.Stream()
+        ms = []
+        for r in range(rounds):
+            h = plan.current_handle()
+            plan.fill(h, views, seed, kind=w["elem"], mark=False, stream=prod)
+            plan.start(prod)
+            plan.mark_all(h, stream=prod)
+            plan.wait(60.0)
+            if r >= 2:
+                ms.append(plan.stats()["engine_ms"])
+            plan.next_round()
+        plan.close()
+        del rep
+        torch.cuda.empty_cache()
+        out.append(round(P * B / (statistics.mean(ms) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+    return out
+
+
 def run_gemm_only(torch, tc, workloads, seed, reps):
     """The P GEMM producers back to back with no plan, `reps` times."""
     from synth import gemm_operands
@@ -415,6 +443,8 @@ def main():
     ap.add_argument("--overlap-cus", type=int, default=0,
                     help="confine the copy engine of the GEMM overlap run to the first N CUs "
                          "(0: every CU, shared with the producer)")
+    ap.add_argument("--placement-trials", type=int, default=0,
+                    help="also measure the copy engine on N fresh allocations of the replicas")
     ap.add_argument("--gemm-only", action="store_true",
                     help="time only the 4 GEMM producers, with no plan (for counter collection)")
     ap.add_argument("--no-extras", action="store_true")
@@ -471,6 +501,10 @@ def main():
         extras["u32_whole_p8_round"] = run_small_round(torch, tc, workloads, BASE_SEED, "u32_whole_p8", 50)
         extras["overlapped_triggered_round"] = {"ms": h.get("overlapped_round_ms"),
                                                 "delivered_gbs": h.get("overlapped_delivered_gbs")}
+    if args.placement_trials:
+        log(f"copy engine on {args.placement_trials} fresh replica allocations")
+        extras["engine_frac_per_allocation"] = run_placement_trials(torch, tc, workloads, BASE_SEED,
+                                                                     args.placement_trials)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: the oracle on a bounded sample")
@@ -499,7 +533,8 @@ def main():
                      "launch_ms_mean": round(h["engine_ms_mean"], 4)},
         "hbm_frac": round(h["achieved"] / HBM_PEAK_GBS, 4),
         "engine_window_ms_median": round(h["window_ms_median"], 4),
-        "overlap_slowdown_pct": round(extras["gemm_overlap"]["slowdown_pct"], 2) if extras else None,
+        "overlap_slowdown_pct": (round(extras["gemm_overlap"]["slowdown_pct"], 2)
+                                 if "gemm_overlap" in extras else None),
         "cpu_baseline": cpu,
         "extras": extras,
     }
