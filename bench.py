@@ -232,12 +232,10 @@ def run_overlap(torch, tc, workloads, seed, reps=40, cu_mask=None, engine_ctas=0
 
 def run_consumer_overlap(torch, tc, workloads, seed, reps=20, N2=256):
     """The 4 GEMM producers' round followed by each rank's in-kernel consumer
-    (Y_q = gathered rows of replica q [8000, 2000] x W [2000, 256]), three ways:
-    consumers launched after wait() returns ("sequential"); queued on the
+    (Y_q = gathered rows of replica q [8000, 2000] x W [2000, 256]), two ways:
+    consumers launched after wait() returns ("sequential"), and queued on the
     producers' stream right behind them, waiting on the device for the
-    chunks still being copied ("chained"); and launched on a stream of their
-    own right after start(), before the producers ("early": their waiting
-    CTAs hold CUs the producers need)."""
+    chunks still being copied ("chained")."""
     from synth import gemm_operands
     import numpy as np
     w = workloads.FULL["gemm_tiles_p4"]
@@ -257,7 +255,7 @@ def run_consumer_overlap(torch, tc, workloads, seed, reps=20, N2=256):
     dp = torch.from_numpy(np.ascontiguousarray(pairs).astype(np.int32).reshape(-1)).cuda()
     Y = [torch.zeros(R * N2, dtype=torch.int16, device="cuda") for _ in range(P)]
     status = torch.zeros((P, len(start) - 1), dtype=torch.int32, device="cuda")
-    prod, cons = torch.cuda.Stream(), torch.cuda.Stream()
+    prod = torch.cuda.Stream()
 
     def producers(h):
         for p in range(P):
@@ -270,14 +268,12 @@ def run_consumer_overlap(torch, tc, workloads, seed, reps=20, N2=256):
             tc.gemm_consume_bf16(h, q, ds, dp, rep[q], wt, Y[q], M=R, N=N2, K=N, status=status[q],
                                  programs=programs, stream=stream)
 
-    times = {"sequential": [], "chained": [], "early": []}
+    times = {"sequential": [], "chained": []}
     for i in range(reps + 2):
         for mode in times:
             torch.cuda.synchronize()
             a = time.perf_counter()
             h = plan.start(prod)
-            if mode == "early":      # half the CUs: the producers must find room
-                consumers(h, cons, 128)
             producers(h)
             if mode == "chained":
                 consumers(h, prod, 256)
@@ -293,7 +289,7 @@ def run_consumer_overlap(torch, tc, workloads, seed, reps=20, N2=256):
     plan.close()
     flops = 2.0 * R * N2 * N * P
     med = {k: statistics.median(v) for k, v in times.items()}
-    return dict(sequential_ms=med["sequential"], chained_ms=med["chained"], early_ms=med["early"],
+    return dict(sequential_ms=med["sequential"], chained_ms=med["chained"],
                 chained_saved_pct=(1 - med["chained"] / med["sequential"]) * 100,
                 consumer_gflop=flops / 1e9, failed_waits=bad)
 

@@ -418,9 +418,12 @@ int tc_plan_row_deps(const tc_plan* plan, const tc_view* view, uint32_t tile_row
  * [dep_start[b], dep_start[b + 1]) -- device copies of tc_plan_row_deps with
  * tile_rows = 128.  status (device, one u32 per row block, may be NULL) gets
  * 2 where a wait ran out of polls; the block is then computed from whatever
- * the rows hold.  On one GPU the simulated ranks share the CUs: a consumer
- * started before its producers must leave them room (programs at most half
- * the CUs), or its waiting CTAs may hold every CU until their polls run out.
+ * the rows hold.  Queue it behind its rank's producers on their stream (or
+ * on any stream after they are queued): HIP maps streams onto a few hardware
+ * queues, so a consumer queued ahead of its producer on another stream may
+ * share that producer's hardware queue and block it until the polls run
+ * out; and on one GPU the simulated ranks share the CUs, so waiting CTAs
+ * hold CUs the producers need.
  * TC_EINVAL as tc_gemm_bf16, or dst >= nranks, max_polls == 0. */
 int tc_gemm_consume_bf16(const tc_handle* h, uint32_t dst, const uint32_t* dep_start,
                          const uint32_t* dep_pairs, uint32_t max_polls, uint32_t* status,

@@ -1,6 +1,7 @@
 """GPU parity of the in-kernel consumer: a GEMM over every rank's replica of
-the gathered rows, started before its producers, waiting per 128-row block
-for the chunks those rows hold (device view wait).  The result must equal the
+the gathered rows, queued right behind its producers, waiting on the device
+per 128-row block for the chunks those rows hold while the copy engine is
+still delivering them.  The result must equal the
 fp32 reference on the gathered rows of the same round (stale rows from the
 round before, or the sentinel, would not), and every wait must succeed.  The
 row dependencies the library computes must contain the oracle's exact set.
@@ -19,7 +20,7 @@ from tests.gpu_common import Pair, log
 
 pytestmark = pytest.mark.gpu
 
-SMALL_CU_SHARE = 64   # consumer programs: leave the producers room on the CUs
+SMALL_CU_SHARE = 64   # consumer programs for the small case
 
 
 def _deps_device(pair, gathered_tv, gathered_ov):
@@ -55,19 +56,18 @@ def test_consumer_waits_for_filled_tiles():
         rng = np.random.default_rng(5)
         wt_bits = (rng.standard_normal((N, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
         wt = torch.from_numpy(wt_bits.view(np.int16)).cuda()
-        cons = torch.cuda.Stream()
         for r in (1, 2):
             log(f"consumer after fill, round {r}")
             Y = [torch.zeros(R * N, dtype=torch.int16, device="cuda") for _ in range(3)]
             status = torch.zeros((3, len(ds) - 1), dtype=torch.int32, device="cuda")
             torch.cuda.synchronize()
             h = pair.plan.start(pair.stream)
-            for q in range(3):   # consumers first: they wait on the device
-                tc.gemm_consume_bf16(h, q, ds, dp, pair.rep[q], wt, Y[q], M=R, N=N, K=K,
-                                     status=status[q], programs=SMALL_CU_SHARE, stream=cons)
             pair.plan.fill(h, pair.tv, pair.seed, kind="bf16", stream=pair.stream)
+            for q in range(3):   # behind the producer: they wait for the engine's copies
+                tc.gemm_consume_bf16(h, q, ds, dp, pair.rep[q], wt, Y[q], M=R, N=N, K=K,
+                                     status=status[q], programs=SMALL_CU_SHARE, stream=pair.stream)
             pair.plan.wait(10.0)
-            cons.synchronize()
+            torch.cuda.synchronize()
             pair.oracle_round()
             pair.compare(f"consumer round {r}")
             X_bits = pair.sim.rep[0][:R * K * 2].view(np.uint16).reshape(R, K)
@@ -97,20 +97,19 @@ def test_consumer_of_gemm_producers():
         for p in range(P):
             a, bt = gemm_operands(BASE_SEED, p, 1, M, N, K)
             ops.append((torch.from_numpy(a.view(np.int16)).cuda(), torch.from_numpy(bt.view(np.int16)).cuda()))
-        cons = torch.cuda.Stream()
         Y = [torch.zeros(R * N2, dtype=torch.int16, device="cuda") for _ in range(P)]
         status = torch.zeros((P, len(ds) - 1), dtype=torch.int32, device="cuda")
         torch.cuda.synchronize()
         h = pair.plan.start(pair.stream)
-        for q in range(P):
-            tc.gemm_consume_bf16(h, q, ds, dp, pair.rep[q], wt, Y[q], M=R, N=N2, K=N,
-                                 status=status[q], programs=128, stream=cons)
         for p in range(P):
             tc.gemm_bf16(ops[p][0], ops[p][1], pair.rep[p][p * M * N * 2:], ldc=N, M=M, N=N,
                          programs=w["programs"], group_m=w["group_m"], handle=h, rank=p,
                          first_chunk=0, tiles_per_chunk=w["tiles_per_chunk"], stream=pair.stream)
+        for q in range(P):
+            tc.gemm_consume_bf16(h, q, ds, dp, pair.rep[q], wt, Y[q], M=R, N=N2, K=N,
+                                 status=status[q], programs=256, stream=pair.stream)
         pair.plan.wait(30.0)
-        cons.synchronize()
+        torch.cuda.synchronize()
         # The gathered rows: each rank's own block as its producer wrote it.
         host = pair.rep.cpu().numpy()
         X_bits = np.concatenate([host[p][p * M * N * 2:(p + 1) * M * N * 2].view(np.uint16)

@@ -170,26 +170,33 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
       const uint32_t kt = 2 * it + grp, cur = it & 1;
       if (kt + 2 < nk) fetch(kt + 2);  // in flight while this slab is multiplied
       if (kt < nk) {
+        // Operand fragment of one 16x16x32 block: lane l holds row (l % 16)
+        // and 8 consecutive k values starting at 8 * (l / 16).  Both 32-wide
+        // k steps' fragments are read first, then the 32 MFMAs run (the
+        // scheduling barrier keeps the compiler from interleaving them back
+        // into read-wait-multiply pairs); the other wave of the SIMD covers
+        // this wave's LDS latency.
         const uint16_t* As = slab(cur);
         const uint16_t* Bs = As + kSlab;
+        const uint32_t fr = lane & 15, fq = 8 * (lane >> 4);
+        bf16x8 fa[2][4], fb[2][4];
 #pragma unroll
-        for (int kk = 0; kk < BK; kk += 32) {
-          // Operand fragment of one 16x16x32 block: lane l holds row
-          // (l % 16) and 8 consecutive k values starting at 8 * (l / 16).
-          const uint32_t fr = lane & 15, fk = kk + 8 * (lane >> 4);
-          bf16x8 fa[4], fb[4];
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            fa[i] = *reinterpret_cast<const bf16x8*>(As + (wm * 64 + i * 16 + fr) * LDA + fk);
+            fa[h][i] = *reinterpret_cast<const bf16x8*>(As + (wm * 64 + i * 16 + fr) * LDA + 32 * h + fq);
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            fb[j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 64 + j * 16 + fr) * LDA + fk);
+            fb[h][j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 64 + j * 16 + fr) * LDA + 32 * h + fq);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-        }
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[h][i], fb[h][j], acc[i][j], 0, 0, 0);
       }
       // The other buffer was last read in the previous iteration, which every
       // wave finished before that iteration's closing barrier.
