@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
           for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[h][i], fb[h][j], acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[h][j], fa[h][i], acc[i][j], 0, 0, 0);
       }
       // The other buffer was last read in the previous iteration, which every
       // wave finished before that iteration's closing barrier.
@@ -214,20 +214,21 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
           *reinterpret_cast<f32x4*>(red + ((gw * 16 + i * 4 + j) * 64 + lane) * 4) = acc[i][j];
     }
     __syncthreads();
-    // Group 0 adds them and stages the tile as bf16.  Output block layout:
-    // lane l holds rows 4 * (l / 16) + e, e = 0..3, of column l % 16.
+    // Group 0 adds them and stages the tile as bf16.  The MFMA takes the B
+    // fragment as its first operand, so its output block is C transposed:
+    // lane l holds row l % 16 and the 4 consecutive columns 4 * (l / 16) + e,
+    // e = 0..3 -- one 8-byte write per block.
     if (grp == 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const f32x4 o = *reinterpret_cast<const f32x4*>(red + ((gw * 16 + i * 4 + j) * 64 + lane) * 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t r = wm * 64 + i * 16 + 4 * (lane >> 4) + e;
-            const uint32_t c = wn * 64 + j * 16 + (lane & 15);
-            cst[r * LDC + c] = (uint16_t)f32_to_bf16_rne(acc[i][j][e] + o[e]);
-          }
+          const uint32_t r = wm * 64 + i * 16 + (lane & 15);
+          const uint32_t c = wn * 64 + j * 16 + 4 * (lane >> 4);
+          const uint32_t lo = f32_to_bf16_rne(acc[i][j][0] + o[0]) | (f32_to_bf16_rne(acc[i][j][1] + o[1]) << 16);
+          const uint32_t hi = f32_to_bf16_rne(acc[i][j][2] + o[2]) | (f32_to_bf16_rne(acc[i][j][3] + o[3]) << 16);
+          *reinterpret_cast<uint2*>(cst + r * LDC + c) = make_uint2(lo, hi);
         }
     }
     __syncthreads();
