@@ -14,24 +14,28 @@
 //    64-lane wave is an independent worker that claims pieces of a source
 //    with an atomic ticket, so consecutive pieces are in flight on different
 //    CUs at once and the addresses in flight stay within a narrow window.
-//  * A wave reading a chunk for the first time polls its gate (low 32 bits of
-//    `ready` >= round).  Data is read with device-scope loads, which return
-//    the coherent copy, so no cache invalidate is needed after the gate.
+//  * A wave reading a chunk for the first time polls its gate: the chunk's
+//    mark count (the sum of its stripes) >= round * writers, or the plan's
+//    force word set by a close() in mid-round.  Data is read with
+//    device-scope loads, which return the coherent copy, so no cache
+//    invalidate is needed after the gate.
 //  * A piece is read once and written to all P-1 other replicas (fan-out): the
 //    P per-peer queues of one source see the same gates, so they advance
 //    together and delivering to all of them at once changes no outcome.
 //    Stores are system-scope write-through, so once the wave's store counter
 //    drains the bytes are visible without an L2 write-back.
-//  * The wave finishing a chunk's last piece signals it: it waits until every
-//    earlier chunk of the same source has been signalled (head-of-line order,
-//    [TP] contract item 1), adds 1 to `arrival` in every receiver's gate row,
-//    and advances the queue cursors.
+//  * Every wave counts its finished piece without waiting for the atomic's
+//    result; the wave holding a chunk's last piece waits for the others'
+//    counts, then until every earlier chunk of the same source has been
+//    signalled (head-of-line order, [TP] contract item 1), then stores the
+//    round into `arrival` in every receiver's gate row and advances the
+//    queue cursors.
 //  * All control flow is wave-uniform; lanes past the end of a piece are
 //    masked by the buffer range check.
 //
-// Every poll loop also watches an abort word in pinned host memory and a
-// wall-clock backstop, so every wave of the engine exits even when a gate
-// never opens.  A round interrupted that way is resumed by launching the
+// Every poll loop also watches a device stop word, an abort word in pinned
+// host memory and a wall-clock backstop, so every wave of the engine exits
+// even when a gate never opens.  A round interrupted that way is resumed by launching the
 // engine again: pieces are re-copied (same bytes), chunks already signalled
 // are not signalled twice.
 #include <hip/hip_ext.h>
