@@ -42,6 +42,15 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def code_only(src):
+    """C/C++ source without comments and with whitespace collapsed, so that
+    editing a comment does not count as changing the kernel."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def counted_traffic(workload, engine_ctas, piece_bytes):
     """HBM bytes per engine launch from the committed FETCH_SIZE/WRITE_SIZE
     summary, or None when the engine sources or the launch differ from the
@@ -55,8 +64,8 @@ def counted_traffic(workload, engine_ctas, piece_bytes):
         text = open(path).read()
         h = hashlib.sha256()
         for f in ENGINE_SOURCES:
-            with open(os.path.join(ROOT, f), "rb") as fh:
-                h.update(fh.read())
+            with open(os.path.join(ROOT, f)) as fh:
+                h.update(code_only(fh.read()).encode())
     except OSError:
         return None
     want = re.search(r"engine_source_sha256: ([0-9a-f]{64})", text)
