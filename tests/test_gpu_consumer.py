@@ -120,3 +120,47 @@ def test_consumer_of_gemm_producers():
         _check_outputs(Y, status, X_bits, wt_bits, "GEMM producers")
     finally:
         pair.close()
+
+
+def test_row_deps_random_schedules():
+    # The library's dependency lists against the oracle's exact sets, on
+    # random small schedules (strided views, 1-D and 2-D pieces, small
+    # pieces that split regions) and random block heights.
+    rng = np.random.default_rng(21)
+    for trial in range(12):
+        P = int(rng.integers(1, 5))
+        rows, cols = int(rng.integers(1, 40)), int(rng.integers(1, 48))
+        e = int(rng.choice([1, 2, 4]))
+        stride = cols + int(rng.integers(0, 4))
+        w = dict(P=P, rows=rows, cols=cols, stride=stride, elem={1: "u8", 2: "bf16", 4: "u32"}[e],
+                 builder="whole", writers=1, rounds=1)
+        pair = Pair(w, oracle_bytes=False, piece_bytes=int(rng.choice([256, 512, 8192])))
+        try:
+            ts, os_ = [], []
+            for p in range(P):
+                kind = int(rng.integers(0, 3))
+                if kind == 0:
+                    ts.append(tc.whole(pair.tv[p], 1))
+                    os_.append(osched.whole(pair.ov[p], 1))
+                elif kind == 1:
+                    n = int(rng.integers(1, rows + 1))
+                    ts.append(tc.chunks(pair.tv[p], n, 1))
+                    os_.append(osched.chunks(pair.ov[p], n, 1))
+                else:
+                    bm, bn, tpc = int(rng.integers(1, 9)), int(rng.integers(1, 9)), int(rng.integers(1, 4))
+                    ts.append(tc.tile_chunks(pair.tv[p], (bm, bn), tpc))
+                    os_.append(osched.tile_chunks(pair.ov[p], bm, bn, tpc, None))
+            pair.plan.close()
+            pair.plan = tc.TriggeredPlan(pair.rep, ts, backstop_s=20.0)
+            pair.os = os_
+            tr = int(rng.integers(1, 20))
+            gtv = tc.View(0, P * rows, cols, stride, e, 0)
+            gov = osched.View(0, P * rows, cols, stride, e)
+            start, pairs = pair.plan.row_deps(gtv, tr)
+            exact = ocons.row_deps(os_, gov, tr)
+            assert len(start) == len(exact) + 1
+            for b, want in enumerate(exact):
+                got = sorted(tuple(int(x) for x in pr) for pr in pairs[start[b]:start[b + 1]])
+                assert got == want, f"trial {trial} block {b}: {got} vs {want}"
+        finally:
+            pair.close()
