@@ -50,9 +50,32 @@ struct FillArgs {
   uint32_t order_stride, G, max_chunks, pad1;
 };
 
-__device__ inline uint64_t key_hash(const FillArgs& a, uint32_t p, uint64_t idx) {
-  const uint64_t k = ((uint64_t)p << 48) | ((uint64_t)a.h.round << 32) | idx;
-  return mix64(k ^ a.seed_mix);
+// mix64(k ^ mix64(seed)) for k = (p << 48) | (round << 32) | idx, idx < 2^32.
+// The high word of the key is the same for every element of a rank, so
+// half of the first 64-bit product is too: with z = k ^ seed_mix split into
+// words (zhi, zlo) and t = z ^ (z >> 30), t * C1 mod 2^64 needs only
+// tlo * C1lo in full plus the low words of tlo * C1hi and thi * C1lo, the
+// last a constant.  Same bits as mix64, one 32-bit multiply fewer.
+struct KeyHash {
+  uint32_t zhi, smlo, thi_c1lo;
+};
+
+__device__ inline KeyHash key_hash_setup(const FillArgs& a, uint32_t p) {
+  KeyHash k;
+  k.zhi = ((p << 16) | a.h.round) ^ (uint32_t)(a.seed_mix >> 32);
+  k.smlo = (uint32_t)a.seed_mix;
+  k.thi_c1lo = (k.zhi ^ (k.zhi >> 30)) * 0x1CE4E5B9u;
+  return k;
+}
+
+__device__ inline uint64_t key_hash(const KeyHash& k, uint32_t idx) {
+  const uint32_t lo = idx ^ k.smlo;
+  const uint32_t tlo = lo ^ ((k.zhi << 2) | (lo >> 30));
+  const uint64_t prod = (uint64_t)tlo * 0x1CE4E5B9u;
+  const uint32_t z1hi = (uint32_t)(prod >> 32) + tlo * 0xBF58476Du + k.thi_c1lo;
+  const uint64_t z1 = ((uint64_t)z1hi << 32) | (uint32_t)prod;
+  const uint64_t z2 = (z1 ^ (z1 >> 27)) * 0x94D049BB133111EBull;
+  return z2 ^ (z2 >> 31);
 }
 
 __device__ inline uint32_t bf16_of(uint64_t h) {
@@ -74,6 +97,7 @@ __device__ inline uint64_t index_at(const FillArgs& a, uint32_t p, uint64_t off)
 __device__ void fill_range(const FillArgs& a, uint32_t p, uint64_t off, uint64_t len) {
   uint8_t* base = reinterpret_cast<uint8_t*>(a.rep[p]);
   const uint64_t idx0 = index_at(a, p, off);
+  const KeyHash kh = key_hash_setup(a, p);
   const uint32_t e = a.elem;
   if (((off | len) & 15) == 0) {
     const uint32_t per = 16 / e;  // elements per 16-byte vector
@@ -84,17 +108,18 @@ __device__ void fill_range(const FillArgs& a, uint32_t p, uint64_t off, uint64_t
       u32x4 out;
       if (a.kind == TC_FILL_U32) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) out[k] = (uint32_t)key_hash(a, p, i0 + k);
+        for (int k = 0; k < 4; ++k) out[k] = (uint32_t)key_hash(kh, (uint32_t)(i0 + k));
       } else if (a.kind == TC_FILL_BF16) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          out[k] = bf16_of(key_hash(a, p, i0 + 2 * k)) | (bf16_of(key_hash(a, p, i0 + 2 * k + 1)) << 16);
+          out[k] = bf16_of(key_hash(kh, (uint32_t)(i0 + 2 * k))) |
+                   (bf16_of(key_hash(kh, (uint32_t)(i0 + 2 * k + 1))) << 16);
       } else {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           uint32_t w = 0;
 #pragma unroll
-          for (int b = 0; b < 4; ++b) w |= ((uint32_t)key_hash(a, p, i0 + 4 * k + b) & 0xFF) << (8 * b);
+          for (int b = 0; b < 4; ++b) w |= ((uint32_t)key_hash(kh, (uint32_t)(i0 + 4 * k + b)) & 0xFF) << (8 * b);
           out[k] = w;
         }
       }
@@ -103,7 +128,7 @@ __device__ void fill_range(const FillArgs& a, uint32_t p, uint64_t off, uint64_t
   } else {
     const uint64_t n = len / e;
     for (uint64_t i = threadIdx.x; i < n; i += kFillThreads) {
-      const uint64_t h = key_hash(a, p, idx0 + i);
+      const uint64_t h = key_hash(kh, (uint32_t)(idx0 + i));
       uint8_t* d = base + off + i * e;
       if (a.kind == TC_FILL_U32) {
         const uint32_t v = (uint32_t)h;
