@@ -3,8 +3,8 @@
 
 A step is one round of the whole path on the 4-rank x 1.5 GiB workload
 (per-rank u32 [786432, 512], three 0.5 GiB row-block chunks, 64 writers
-each): the producer writes every rank's block, the round starts, the
-writers' marks open the gates, the copy engine delivers every chunk to the
+each): the producer (a persistent grid taking the writer slots) writes
+every rank's block, the round starts, the writers' marks open the gates, the copy engine delivers every chunk to the
 three other replicas and signals its arrivals, wait() checks completion,
 next_round() re-arms.  Marks are deferred (issued by a mark kernel after the
 fill), so the copy engine's window holds no producer traffic.
@@ -107,7 +107,7 @@ def run_headline(args, torch, tc, workloads, seed):
 
     def step(record):
         h = plan.current_handle()
-        plan.fill(h, views, seed, kind=w["elem"], mark=False, stream=prod)
+        plan.fill(h, views, seed, kind=w["elem"], mark=False, waves=True, stream=prod)
         if args.premark:
             # Profiling order: the marks precede start(), so no kernel ever
             # waits on a kernel queued after it (a profiler that runs kernels

@@ -353,7 +353,7 @@ typedef struct tc_fill_desc {
   uint32_t rsvd;
   const uint32_t* order;  /* device, [P][max_chunks] when SERIAL; NULL = schedule order */
   uint32_t order_stride;  /* entries per rank in order[] */
-  uint32_t ctas;          /* WAVES: persistent grid size (0 = three CTAs per CU); else 0 */
+  uint32_t ctas;          /* WAVES: persistent grid size (0 = two CTAs per CU); else 0 */
 } tc_fill_desc;
 
 /* Hash-fill producer for every rank's chunks of `plan`, on `stream`.

@@ -46,9 +46,13 @@ struct ChunkD {
   uint32_t npieces;
   uint64_t bytes;        // payload bytes of the chunk
   uint32_t writers;
-  uint32_t pad;
+  uint32_t flags;        // kChunkContiguous
 };
 static_assert(sizeof(ChunkD) == 32, "chunk descriptor is 32 bytes");
+
+// The chunk's pieces are all one row and each starts where the one before
+// ends: the chunk is one contiguous byte range.
+constexpr uint32_t kChunkContiguous = 1;
 
 // Cuts every rank's regions into pieces of about piece_bytes (whole rows for
 // 2-D regions; a linear region into piece_bytes ranges).

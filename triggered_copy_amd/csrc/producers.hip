@@ -148,11 +148,20 @@ __device__ void fill_piece(const FillArgs& a, uint32_t p, const tc::PieceD& pc) 
   for (uint32_t r = 0; r < pc.rows; ++r) fill_range(a, p, pc.off + (uint64_t)r * pc.pitch, pc.row_bytes);
 }
 
-// Writer j of chunk g writes pieces [j*np/w, (j+1)*np/w) of the chunk.
+// Writer j of chunk g writes pieces [j*np/w, (j+1)*np/w) of the chunk: as
+// one byte range when the chunk is contiguous in a contiguous view (no
+// per-piece descriptor round trips), else piece by piece.
 __device__ void fill_share(const FillArgs& a, uint32_t g, uint32_t j) {
   const tc::ChunkD cd = a.chunks[g];
   const uint64_t lo = (uint64_t)j * cd.npieces / cd.writers;
   const uint64_t hi = (uint64_t)(j + 1) * cd.npieces / cd.writers;
+  if (lo == hi) return;
+  if ((cd.flags & tc::kChunkContiguous) && (a.contiguous & (1u << cd.rank))) {
+    const tc::PieceD first = a.pieces[cd.first_piece + lo];
+    const tc::PieceD last = a.pieces[cd.first_piece + hi - 1];
+    fill_range(a, cd.rank, first.off, last.off + last.row_bytes - first.off);
+    return;
+  }
   for (uint64_t k = lo; k < hi; ++k) fill_piece(a, cd.rank, a.pieces[cd.first_piece + k]);
 }
 
@@ -316,10 +325,10 @@ int tc_produce_fill(tc_plan* P, const tc_handle* h, const tc_fill_desc* d, void*
   } else if (d->mode == TC_FILL_WAVES) {
     if (P->total_writers == 0) return TC_OK;
     uint32_t ctas = d->ctas;
-    if (ctas == 0) {  // three 4-wave CTAs per CU: the hash fill needs them to keep the ALUs busy
+    if (ctas == 0) {  // two 4-wave CTAs per CU: the measured optimum for the hash fill
       int cus = 0;
       TC_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, P->device));
-      ctas = 3u * (uint32_t)cus;
+      ctas = 2u * (uint32_t)cus;
     }
     for (uint32_t p = 0; p < P->P; ++p)
       a.max_chunks = std::max(a.max_chunks, P->chunk_base[p + 1] - P->chunk_base[p]);

@@ -337,6 +337,12 @@ void tc::build_pieces(uint32_t nranks, const tc_schedule* const* sched, uint64_t
         }
       }
       cd.npieces = (uint32_t)pieces.size() - cd.first_piece;
+      bool contiguous = cd.npieces > 0;
+      for (uint32_t i = cd.first_piece; i < cd.first_piece + cd.npieces && contiguous; ++i)
+        contiguous = pieces[i].rows == 1 &&
+                     (i == cd.first_piece ||
+                      pieces[i].off == pieces[i - 1].off + pieces[i - 1].row_bytes);
+      if (contiguous) cd.flags |= kChunkContiguous;
       chunks.push_back(cd);
     }
   }
