@@ -356,10 +356,27 @@ def run_gemm_only(torch, tc, workloads, seed, reps):
         if i >= 2:
             ts.append(e0.elapsed_time(e1))
     ms = statistics.median(ts)
+    # The library GEMM (torch.mm, hipBLASLt) on the same operands and shape,
+    # for context: C = A @ B with B given as its transpose Bt [N, K].
+    bf = torch.bfloat16
+    lib_out = [torch.empty(M, N, dtype=bf, device="cuda") for _ in range(P)]
+    lts = []
+    with torch.cuda.stream(prod):
+        for i in range(reps + 2):
+            torch.cuda.synchronize()
+            e0.record(prod)
+            for p in range(P):
+                torch.mm(ops[p][0].view(bf).view(M, K), ops[p][1].view(bf).view(N, K).t(), out=lib_out[p])
+            e1.record(prod)
+            e1.synchronize()
+            if i >= 2:
+                lts.append(e0.elapsed_time(e1))
+    lib_ms = statistics.median(lts)
     flops = 2.0 * M * N * K * P
     return {"metric": "bf16 GEMM producer (M=N=2000, K=1024, 4 ranks back to back)",
             "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
-            "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "reps": reps}
+            "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "reps": reps,
+            "library_mm_ms": lib_ms, "library_mm_tflops": flops / (lib_ms * 1e-3) / 1e12}
 
 
 def run_barrier(torch, tc, workloads):
