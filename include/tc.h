@@ -207,8 +207,10 @@ typedef struct tc_plan_desc {
   uint64_t rows_per_rank_bytes;        /* for TC_CHECK_OWN_ROWS */
   const uint32_t* cu_mask;             /* NULL = copy engine may use every CU */
   uint32_t cu_mask_words;
-  uint32_t engine_ctas;                /* CTAs of 4 worker waves; 0 = one wave per 64 KiB of
-                                          source bytes per round, at most 16 waves per usable CU */
+  uint32_t engine_ctas;                /* CTAs of 4 worker waves; 0 = one wave per 192 KiB of
+                                          delivered bytes per round (source bytes times the
+                                          P - 1 receivers), at least one per piece up to 256,
+                                          at most 16 waves per usable CU */
   uint64_t piece_bytes;                /* copy work unit, multiple of 256, <= 1 GiB; 0 = 8 KiB */
   uint64_t engine_backstop_us;         /* engine gives up after this long; 0 = 30 s */
 } tc_plan_desc;
