@@ -14,7 +14,7 @@ import torch
 import triggered_copy_amd as tc
 from oracle import barrier as obarrier
 from oracle import plan as oplan
-from synth import workloads
+from synth import BASE_SEED, workloads
 from tests.gpu_common import Pair, log, require_gpu, wait_until
 
 pytestmark = pytest.mark.gpu
@@ -216,6 +216,66 @@ def test_hand_built_schedules():
             os_.append(osched.from_tables(chunks, regions))
         _swap_in(pair, ts, os_)
         _rounds(pair, 2, "hand-built")
+    finally:
+        pair.close()
+
+
+def _random_tables(rng, base, rows, cols):
+    """A random hand-built table over one rank's rows [base, base + rows*cols)
+    of a u8 view: the rows cut into bands, each band one region (a 2-D window
+    of some columns, or a linear range that may cross row ends), the regions
+    shuffled and grouped into chunks of 1-3 regions with 1-3 writers."""
+    cuts = sorted(rng.choice(np.arange(1, rows), size=min(rows - 1, int(rng.integers(1, 6))),
+                             replace=False).tolist())
+    regions = []
+    for r0, r1 in zip([0] + cuts, cuts + [rows]):
+        if rng.random() < 0.5:
+            c0 = int(rng.integers(0, cols))
+            width = int(rng.integers(1, cols - c0 + 1))
+            if rng.random() < 0.5 and cols % 16 == 0:       # the engine's 16-byte vector path
+                c0 = c0 // 16 * 16
+                width = max(16, width // 16 * 16) if c0 + 16 <= cols else cols - c0
+            regions.append((base + r0 * cols + c0, r1 - r0, width, cols))
+        else:
+            band = (r1 - r0) * cols
+            a = int(rng.integers(0, band))
+            regions.append((base + r0 * cols + a, 1, int(rng.integers(1, band - a + 1)), 0))
+    regions = [regions[i] for i in rng.permutation(len(regions))]
+    chunks, at = [], 0
+    while at < len(regions):
+        n = min(int(rng.integers(1, 4)), len(regions) - at)
+        chunks.append((at, n, int(rng.integers(1, 4))))
+        at += n
+    return chunks, regions
+
+
+@pytest.mark.parametrize("case", range(32))
+def test_random_hand_built_tables(case):
+    # Random region tables (unaligned 2-D windows, 16-byte aligned ones,
+    # linear ranges across row ends), random chunking and writers, random
+    # piece sizes and engine sizes: bit-exact with the oracle over 2 rounds.
+    from oracle import schedule as osched
+    rng = np.random.default_rng(1000 + case)
+    P = int(rng.integers(2, 6))
+    cols = int(rng.choice([16, 48, 64, int(rng.integers(5, 90))]))
+    rows = int(rng.integers(3, 40))
+    w = dict(P=P, rows=rows, cols=cols, elem="u8", builder="whole", writers=1, rounds=2)
+    pair = Pair(w, seed=BASE_SEED + case)
+    try:
+        ts, os_ = [], []
+        for p in range(P):
+            if P > 2 and rng.random() < 0.15:           # a rank that sends nothing
+                ts.append(None)
+                os_.append(None)
+                continue
+            chunks, regions = _random_tables(rng, p * rows * cols, rows, cols)
+            ts.append(tc.from_arrays(chunks, regions))
+            os_.append(osched.from_tables(chunks, regions))
+        kw = dict(piece_bytes=int(rng.choice([256, 512, 1024, 8192])),
+                  engine_ctas=int(rng.integers(1, 9)))
+        log(f"random tables case {case}: P={P} rows={rows} cols={cols} {kw}")
+        _swap_in(pair, ts, os_, **kw)
+        _rounds(pair, 2, f"random tables case {case}")
     finally:
         pair.close()
 
