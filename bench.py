@@ -523,6 +523,19 @@ def main():
         extras["u32_whole_p8_round"] = run_small_round(torch, tc, workloads, BASE_SEED, "u32_whole_p8", 50)
         extras["overlapped_triggered_round"] = {"ms": h.get("overlapped_round_ms"),
                                                 "delivered_gbs": h.get("overlapped_delivered_gbs")}
+        if args.workload == "u32_chunks_1p5g_p4":
+            # The same buffers as one whole() chunk per rank: regions of 1 GiB
+            # and 0.5 GiB (the 1 GiB split), 192 writers.
+            log("the 1.5 GiB workload as whole(): 1 GiB + 0.5 GiB regions")
+            import copy
+            a2 = copy.copy(args)
+            a2.workload, a2.steps, a2.warmup, a2.no_extras, a2.premark = \
+                "u32_whole_1p5g_p4", 5, 1, True, False
+            hw = run_headline(a2, torch, tc, workloads, BASE_SEED)
+            extras["u32_whole_1p5g_p4"] = {
+                "value_gbs": round(hw["value"], 2), "ms_per_step": round(hw["ms_per_step"], 4),
+                "engine_ms_mean": round(hw["engine_ms_mean"], 4),
+                "engine_frac": round(hw["achieved"] / HBM_PEAK_GBS, 4), "engine_ctas": hw["engine_ctas"]}
     if args.placement_trials:
         log(f"copy engine on {args.placement_trials} fresh replica allocations")
         extras["engine_frac_per_allocation"] = run_placement_trials(torch, tc, workloads, BASE_SEED,
