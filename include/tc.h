@@ -237,6 +237,9 @@ int tc_plan_validate(const tc_plan_desc* desc);
  * producer work it depends on.
  * All-or-nothing ([TP] contract): on failure nothing is kept and *out = NULL.
  * The replicas and workspace must stay allocated, unmoved, until close.
+ * Each replica (buffer_bytes) and the workspace (workspace_bytes) must lie in
+ * one device allocation of the current device: a host pointer or a pointer of
+ * another device gives TC_EINVAL, a size past the allocation's end TC_EBOUNDS.
  * Errors: TC_EINVAL, TC_EBOUNDS, TC_EOVERLAP, TC_ENOMEM, TC_EHIP, TC_ENODEV. */
 int tc_plan_create(const tc_plan_desc* desc, tc_plan** out);
 

@@ -454,6 +454,48 @@ def test_create_rejects_overlap_and_small_workspace():
         tc.TriggeredPlan(rep, [mine[1], mine[0]], own_rows_bytes=2048)
 
 
+def test_create_checks_replica_and_workspace_memory():
+    # Through the C-ABI: a replica in host memory, a replica size past the end
+    # of its allocation, and a workspace size past the end of its allocation
+    # are refused at create time; the same call with good memory succeeds.
+    import ctypes as C
+    from triggered_copy_amd import _lib
+    require_gpu()
+    B = 4096
+    rep = torch.zeros((2, B), dtype=torch.uint8, device="cuda")
+    scheds = [tc.whole(tc.View(p * 2048, 1, 2048, 2048, 1, 0)) for p in range(2)]
+    need = C.c_uint64()
+    sp = (C.c_void_p * 2)(*[s_.ptr.value for s_ in scheds])
+    assert tc.lib().tc_plan_workspace_bytes(2, sp, 0, C.byref(need)) == _lib.OK
+    ws = torch.zeros(need.value, dtype=torch.uint8, device="cuda")
+    host = torch.zeros(B, dtype=torch.uint8).pin_memory()
+
+    def create(reps, buffer_bytes=B, ws_bytes=need.value):
+        rp = (C.c_void_p * 2)(*reps)
+        d = _lib.PlanDesc()
+        d.nranks, d.flags = 2, 0
+        d.replicas = C.cast(rp, C.POINTER(C.c_void_p))
+        d.buffer_bytes = buffer_bytes
+        d.schedules = C.cast(sp, C.POINTER(C.c_void_p))
+        d.workspace, d.workspace_bytes = ws.data_ptr(), ws_bytes
+        d.engine_backstop_us = 20_000_000
+        out = C.c_void_p()
+        rc = tc.lib().tc_plan_create(C.byref(d), C.byref(out))
+        return rc, out
+
+    good = [rep[0].data_ptr(), rep[1].data_ptr()]
+    rc, _ = create([good[0], host.data_ptr()])
+    assert rc == _lib.EINVAL, tc.lib().tc_last_error()
+    rc, _ = create(good, buffer_bytes=1 << 40)
+    assert rc == _lib.EBOUNDS, tc.lib().tc_last_error()
+    rc, _ = create(good, ws_bytes=1 << 40)
+    assert rc == _lib.EBOUNDS, tc.lib().tc_last_error()
+    rc, out = create(good)
+    assert rc == _lib.OK, tc.lib().tc_last_error()
+    closing = C.c_int(0)
+    assert tc.lib().tc_plan_close(out, C.byref(closing)) == _lib.OK
+
+
 def test_barrier_p8_thousand_generations():
     require_gpu()
     w = workloads.FULL["barrier_p8"]

@@ -675,6 +675,30 @@ static void destroy(tc_plan* P) {
   delete P;
 }
 
+// TC_OK when [p, p + bytes) lies in one device allocation of `device`;
+// otherwise an error naming `what`.  A wrong pointer or size then fails here
+// rather than as a memory fault in the copy engine.
+static int check_device_range(const void* p, uint64_t bytes, int device, const char* what) {
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(TC_EINVAL, std::string(what) + " is not memory the HIP runtime knows");
+  }
+  if (attr.type != hipMemoryTypeDevice || attr.device != device)
+    return fail(TC_EINVAL, std::string(what) + " is not device memory of the current device " +
+                               std::to_string(device));
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, const_cast<void*>(p)) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(TC_EINVAL, std::string(what) + ": allocation range unknown");
+  }
+  if ((uintptr_t)p + bytes > (uintptr_t)base + size)
+    return fail(TC_EBOUNDS, std::string(what) + ": " + std::to_string(bytes) +
+                                " bytes run past the end of its allocation");
+  return TC_OK;
+}
+
 int tc_plan_create(const tc_plan_desc* d, tc_plan** out) {
   if (!out) return fail(TC_EINVAL, "out is NULL");
   *out = nullptr;
@@ -686,6 +710,15 @@ int tc_plan_create(const tc_plan_desc* d, tc_plan** out) {
   if ((uintptr_t)d->workspace & 255) return fail(TC_EINVAL, "workspace must be 256-byte aligned");
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev == 0) return fail(TC_ENODEV, "no GPU visible");
+  {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(TC_EHIP, "hipGetDevice failed");
+    for (uint32_t p = 0; p < d->nranks; ++p)
+      if (int rc = check_device_range(d->replicas[p], d->buffer_bytes, dev,
+                                      ("replica " + std::to_string(p)).c_str()))
+        return rc;
+    if (int rc = check_device_range(d->workspace, d->workspace_bytes, dev, "workspace")) return rc;
+  }
 
   auto* P = new tc_plan();
   P->P = d->nranks;
