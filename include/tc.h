@@ -390,7 +390,9 @@ int tc_mark(tc_plan* plan, const tc_handle* h, uint32_t rank, uint32_t chunk,
  * C is stored with system-scope write-through stores, so its marks need no
  * L2 write-back (tc_mark_ready_wt).
  * TC_EINVAL unless K % 8 == 0, N % 8 == 0, ldc % 8 == 0, ldc < 2^23, pointers
- * 16-byte aligned. */
+ * 16-byte aligned, and A, Bt, C device memory of the current device;
+ * TC_EBOUNDS when A ((M - 1) * K + K elements), Bt (N * K) or C
+ * ((M - 1) * ldc + N) runs past the end of its allocation. */
 int tc_gemm_bf16(const void* A, const void* Bt, void* C, uint32_t M, uint32_t N, uint32_t K,
                  uint64_t ldc, uint32_t programs, uint32_t group_m, const tc_handle* h,
                  uint32_t rank, uint32_t first_chunk, uint32_t tiles_per_chunk, void* stream);
@@ -429,7 +431,9 @@ int tc_plan_row_deps(const tc_plan* plan, const tc_view* view, uint32_t tile_row
  * share that producer's hardware queue and block it until the polls run
  * out; and on one GPU the simulated ranks share the CUs, so waiting CTAs
  * hold CUs the producers need.
- * TC_EINVAL as tc_gemm_bf16, or dst >= nranks, max_polls == 0. */
+ * TC_EINVAL / TC_EBOUNDS as tc_gemm_bf16 (with X spanning (M - 1) * ldx + K
+ * elements), and for dep_start (nblocks + 1 words) and status (nblocks
+ * words) likewise; TC_EINVAL for dst >= nranks or max_polls == 0. */
 int tc_gemm_consume_bf16(const tc_handle* h, uint32_t dst, const uint32_t* dep_start,
                          const uint32_t* dep_pairs, uint32_t max_polls, uint32_t* status,
                          const void* X, uint64_t ldx, const void* Wt, void* Y, uint32_t M,

@@ -44,6 +44,27 @@ def test_gemm_matches_reference(M, N, K, programs, group_m):
     assert ok, (worst, frob)
 
 
+def test_gemm_checks_operand_memory():
+    # Operands are checked on the host before the launch: a C in host memory
+    # is refused, and so is a shape whose rows run past an operand's
+    # allocation (M far beyond what A holds).
+    require_gpu()
+    M, N, K = 64, 64, 64
+    a, bt = gemm_operands(BASE_SEED, 0, 1, M, N, K)
+    A, Bt = _u16_to_dev(a), _u16_to_dev(bt)
+    host_c = torch.zeros((M, N), dtype=torch.int16).pin_memory()
+    with pytest.raises(tc.InvalidArgument):
+        tc.gemm_bf16(A, Bt, host_c)
+    C_out = torch.zeros((M, N), dtype=torch.int16, device="cuda")
+    with pytest.raises(tc.BoundsError):
+        tc.gemm_bf16(A, Bt, C_out, M=(1 << 32) - 1)
+    tc.gemm_bf16(A, Bt, C_out)
+    torch.cuda.synchronize()
+    got = ogemm.bf16_bits_to_f32(C_out.cpu().numpy().view(np.uint16))
+    ok, worst, frob = ogemm.within_tolerance(got, ogemm.gemm_ref(a, bt), 1e-2)
+    assert ok, (worst, frob)
+
+
 def test_gemm_tiles_p4_full():
     w = workloads.FULL["gemm_tiles_p4"]
     pair = Pair(w)

@@ -270,6 +270,11 @@ static int check_gemm_shape(const void* A, const void* Bt, const void* C, uint32
     return fail(TC_EINVAL, "gemm: a 128-row tile of C must span less than 2 GiB (ldc < 2^23)");
   if (((uintptr_t)A | (uintptr_t)Bt | (uintptr_t)C) & 15)
     return fail(TC_EINVAL, "gemm: operands must be 16-byte aligned");
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(TC_EHIP, "gemm: hipGetDevice failed");
+  if (int rc = tc::check_device_range(A, ((uint64_t)(M - 1) * lda + K) * 2, dev, "gemm: A")) return rc;
+  if (int rc = tc::check_device_range(Bt, (uint64_t)N * K * 2, dev, "gemm: Bt")) return rc;
+  if (int rc = tc::check_device_range(C, ((uint64_t)(M - 1) * ldc + N) * 2, dev, "gemm: C")) return rc;
   return TC_OK;
 }
 
@@ -327,6 +332,15 @@ extern "C" int tc_gemm_consume_bf16(const tc_handle* h, uint32_t dst, const uint
   if (dst >= h->nranks) return fail(TC_EINVAL, "consume gemm: dst out of range");
   if (max_polls == 0) return fail(TC_EINVAL, "consume gemm: max_polls is 0");
   if (int rc = check_gemm_shape(X, Wt, Y, M, N, K, ldx, ldy, programs, group_m)) return rc;
+  {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(TC_EHIP, "consume gemm: hipGetDevice failed");
+    const uint64_t nb = (M + BM - 1) / BM;
+    if (int rc = tc::check_device_range(dep_start, (nb + 1) * 4, dev, "consume gemm: dep_start"))
+      return rc;
+    if (status)
+      if (int rc = tc::check_device_range(status, nb * 4, dev, "consume gemm: status")) return rc;
+  }
   GemmArgs a{};
   fill_shape(a, X, Wt, Y, M, N, K, ldx, ldy, group_m);
   a.h = *h;

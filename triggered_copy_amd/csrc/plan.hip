@@ -675,10 +675,11 @@ static void destroy(tc_plan* P) {
   delete P;
 }
 
+extern "C++" {
 // TC_OK when [p, p + bytes) lies in one device allocation of `device`;
-// otherwise an error naming `what`.  A wrong pointer or size then fails here
-// rather than as a memory fault in the copy engine.
-static int check_device_range(const void* p, uint64_t bytes, int device, const char* what) {
+// otherwise an error naming `what`.  A wrong pointer or size then fails on
+// the host rather than as a memory fault in a kernel.
+int tc::check_device_range(const void* p, uint64_t bytes, int device, const char* what) {
   hipPointerAttribute_t attr{};
   if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
     (void)hipGetLastError();
@@ -698,6 +699,7 @@ static int check_device_range(const void* p, uint64_t bytes, int device, const c
                                 " bytes run past the end of its allocation");
   return TC_OK;
 }
+}  // extern "C++"
 
 int tc_plan_create(const tc_plan_desc* d, tc_plan** out) {
   if (!out) return fail(TC_EINVAL, "out is NULL");

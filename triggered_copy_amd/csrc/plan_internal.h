@@ -87,4 +87,5 @@ struct tc_plan {
 namespace tc {
 void fill_handle(const tc_plan* P, tc_handle* h);
 int hip_fail(hipError_t e, const char* what);
+int check_device_range(const void* p, uint64_t bytes, int device, const char* what);
 }  // namespace tc
