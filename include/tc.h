@@ -357,7 +357,7 @@ typedef struct tc_fill_desc {
   uint32_t mode;          /* TC_FILL_PARALLEL / TC_FILL_SERIAL / TC_FILL_WAVES */
   uint32_t rsvd;
   const uint32_t* order;  /* device, [P][max_chunks] when SERIAL; NULL = schedule order */
-  uint32_t order_stride;  /* entries per rank in order[] */
+  uint32_t order_stride;  /* entries per rank in order[], at least a rank's chunk count */
   uint32_t ctas;          /* WAVES: persistent grid size (0 = two CTAs per CU); else 0 */
 } tc_fill_desc;
 
@@ -365,7 +365,9 @@ typedef struct tc_fill_desc {
  * Writes replica p only (rank p's regions).  With TC_MARK_INKERNEL the plan
  * must be STARTED; with TC_MARK_NONE it may also be READY (data written
  * before start(), marked after it).  TC_EINVAL on a kind / view / order
- * mismatch; TC_ESTATE when h is not the plan's current round. */
+ * mismatch or an order array that is not device memory of the plan's
+ * device; TC_EBOUNDS when P * order_stride words run past its allocation;
+ * TC_ESTATE when h is not the plan's current round. */
 int tc_produce_fill(tc_plan* plan, const tc_handle* h, const tc_fill_desc* d, void* stream);
 
 /* Deferred marks: every chunk of every rank receives exactly its writers'
@@ -401,7 +403,9 @@ int tc_gemm_bf16(const void* A, const void* Bt, void* C, uint32_t M, uint32_t N,
  * 5): one CTA per chunk of every rank; each waits with tc_wait (dst = the
  * given rank, at most max_polls polls) and then copies the chunk's bytes from
  * replica dst into out_buf at the same offsets.  status[g] (device, one u32
- * per global chunk) = 1 when it arrived and was copied, 2 when polls ran out. */
+ * per global chunk) = 1 when it arrived and was copied, 2 when polls ran out.
+ * out_buf (buffer_bytes) and status (G words) must be device memory of the
+ * plan's device within their allocations (TC_EINVAL, TC_EBOUNDS). */
 int tc_consume_copy(tc_plan* plan, const tc_handle* h, uint32_t dst, void* out_buf,
                     uint32_t max_polls, uint32_t* status, void* stream);
 
@@ -454,7 +458,9 @@ int tc_gemm_consume_bf16(const tc_handle* h, uint32_t dst, const uint32_t* dep_s
  *        x[g % 2][(m + 1) % P] (the data reveal: y[r] = x[(r+1) % N]);
  *   snap int32 [n_gen][P][P]: rank m's row W[m][*] right after its waits.
  * status: device u32, set to 1 + rank when a wait ran out of polls (the
- * kernel still exits).  Asynchronous on `stream`. */
+ * kernel still exits).  Asynchronous on `stream`.  Every array given must be
+ * device memory of the current device spanning its size (TC_EINVAL,
+ * TC_EBOUNDS). */
 int tc_barrier_run(int32_t* W, uint32_t P, uint32_t first_gen, uint32_t n_gen,
                    int32_t* x, int32_t* y, int32_t* snap, uint32_t max_polls,
                    uint32_t* status, void* stream);

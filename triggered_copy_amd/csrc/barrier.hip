@@ -83,6 +83,17 @@ extern "C" int tc_barrier_run(int32_t* W, uint32_t P, uint32_t first_gen, uint32
   if (first_gen == 0) return fail(TC_EINVAL, "barrier: generations start at 1");
   if ((uint64_t)first_gen + n_gen > (1u << 23)) return fail(TC_EINVAL, "barrier: generation overflow");
   if (n_gen == 0) return TC_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(TC_EHIP, "barrier: hipGetDevice failed");
+  const uint64_t pp = (uint64_t)P * P * 4;
+  if (int rc = tc::check_device_range(W, pp, dev, "barrier: W")) return rc;
+  if (int rc = tc::check_device_range(status, 4, dev, "barrier: status")) return rc;
+  if (x)
+    if (int rc = tc::check_device_range(x, 2ull * P * 4, dev, "barrier: x")) return rc;
+  if (y)
+    if (int rc = tc::check_device_range(y, (uint64_t)n_gen * P * 4, dev, "barrier: y")) return rc;
+  if (snap)
+    if (int rc = tc::check_device_range(snap, (uint64_t)n_gen * pp, dev, "barrier: snap")) return rc;
   BarrierArgs a{W, x, y, snap, status, P, first_gen, n_gen, max_polls};
   hipLaunchKernelGGL(barrier_kernel, dim3(P), dim3(64), 0, (hipStream_t)stream, a);
   const hipError_t e = hipGetLastError();

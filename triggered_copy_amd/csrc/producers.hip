@@ -316,6 +316,14 @@ int tc_produce_fill(tc_plan* P, const tc_handle* h, const tc_fill_desc* d, void*
   hipStream_t s = (hipStream_t)stream;
   if (d->mode != TC_FILL_WAVES && d->ctas) return fail(TC_EINVAL, "fill: ctas is for the waves mode");
   if (d->mode != TC_FILL_SERIAL && d->order) return fail(TC_EINVAL, "fill: an order needs serial mode");
+  if (d->order) {  // the kernel reads order[p * order_stride + k] for k below rank p's chunk count
+    uint32_t most = 0;
+    for (uint32_t p = 0; p < P->P; ++p) most = std::max(most, P->chunk_base[p + 1] - P->chunk_base[p]);
+    if (d->order_stride < most) return fail(TC_EINVAL, "fill: order_stride below a rank's chunk count");
+    if (int rc = tc::check_device_range(d->order, (uint64_t)P->P * d->order_stride * 4, P->device,
+                                        "fill: order"))
+      return rc;
+  }
   if (d->mode == TC_FILL_SERIAL) {
     hipLaunchKernelGGL(fill_serial_kernel, dim3(P->P), dim3(kFillThreads), 0, s, a);
   } else if (d->mode == TC_FILL_PARALLEL) {
@@ -377,6 +385,10 @@ int tc_consume_copy(tc_plan* P, const tc_handle* h, uint32_t dst, void* out_buf,
   if (!P || !h || !out_buf || !status) return fail(TC_EINVAL, "consume: NULL argument");
   if (dst >= P->P) return fail(TC_EINVAL, "consume: dst out of range");
   if (P->G == 0) return TC_OK;
+  if (int rc = tc::check_device_range(out_buf, P->buffer_bytes, P->device, "consume: out_buf"))
+    return rc;
+  if (int rc = tc::check_device_range(status, (uint64_t)P->G * 4, P->device, "consume: status"))
+    return rc;
   ConsumeArgs a{};
   a.h = *h;
   a.rep_dst = (uint64_t)P->rep[dst];
