@@ -38,6 +38,14 @@ def test_library_exports_every_declared_function():
     assert b"gfx950" in lib.tc_version()
 
 
+def test_header_is_plain_c_and_a_c_program_links(tmp_path):
+    # include/tc.h is usable from C: the C round-trip program compiles with
+    # -Werror and links against the library and the HIP runtime.
+    from tests import c_abi_build
+    exe = c_abi_build.build(str(tmp_path))
+    assert os.path.exists(exe)
+
+
 def _oview(v):
     return osched.View(v.byte_offset, v.rows, v.cols, v.row_stride, v.elem_bytes)
 
