@@ -251,6 +251,8 @@ class TriggeredPlan:
         for r in reps:
             if r.numel() * r.element_size() != nbytes or not r.is_cuda:
                 raise InvalidArgument("replicas must be CUDA tensors of equal size")
+            if not r.is_contiguous() or r.device != reps[0].device:
+                raise InvalidArgument("replicas must be contiguous and on one device")
         self.P, self.buffer_bytes = P, nbytes
         self._keep = (reps, list(schedules))
         sched_ptrs = (C.c_void_p * P)(*[s.ptr.value if s is not None else None for s in schedules])
@@ -281,7 +283,8 @@ class TriggeredPlan:
         d.engine_backstop_us = int(backstop_s * 1e6)
         self._desc = d
         ptr = C.c_void_p()
-        _check(lib().tc_plan_create(C.byref(d), C.byref(ptr)))
+        with torch.cuda.device(reps[0].device):  # the plan's streams live on the replicas' device
+            _check(lib().tc_plan_create(C.byref(d), C.byref(ptr)))
         self._p = ptr
         self.handle = None
 
@@ -454,6 +457,8 @@ def gemm_bf16(A, Bt, C_out, *, ldc=None, programs=256, group_m=8, handle=None, r
               first_chunk=0, tiles_per_chunk=256, M=None, N=None, stream=None):
     """C_out[M, N] (row stride ldc) = A[M, K] @ Bt[N, K].T in bf16 / fp32 acc.
     ``C_out`` may be any CUDA tensor whose data_ptr is the tile origin."""
+    if not (A.is_contiguous() and Bt.is_contiguous()):
+        raise InvalidArgument("gemm_bf16: A and Bt must be contiguous (row-major, K innermost)")
     M = M or A.shape[0]
     K = A.shape[1]
     N = N or Bt.shape[0]
