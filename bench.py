@@ -399,7 +399,10 @@ def run_barrier(torch, tc, workloads):
     return dict(us_per_generation=statistics.median(res), P=P, generations=G)
 
 
-def run_small_round(torch, tc, workloads, seed, name, rounds):
+def run_small_round(torch, tc, workloads, seed, name, rounds, premark=False):
+    """Full rounds of a small workload: start, the fill with in-kernel marks,
+    wait.  With premark (for counter collection, which runs kernels one at
+    a time) the fill and its marks precede start()."""
     w = workloads.FULL[name]
     views, rep, B = rank_setup(w, torch, tc)
     plan = tc.TriggeredPlan(rep, build_sched(w, views, tc))
@@ -407,8 +410,14 @@ def run_small_round(torch, tc, workloads, seed, name, rounds):
     times = []
     for i in range(rounds + 5):
         a = time.perf_counter()
-        h = plan.start(prod)
-        plan.fill(h, views, seed, kind=w["elem"], mark=True, stream=prod)
+        if premark:
+            h = plan.current_handle()
+            plan.fill(h, views, seed, kind=w["elem"], mark=False, stream=prod)
+            plan.mark_all(h, stream=prod)
+            plan.start(prod)
+        else:
+            h = plan.start(prod)
+            plan.fill(h, views, seed, kind=w["elem"], mark=True, stream=prod)
         plan.wait(30.0)
         plan.next_round()
         if i >= 5:
@@ -476,6 +485,9 @@ def main():
                     help="also run an elementwise kernel reading and writing 1 GiB each, "
                          "the reference for scaling HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--small-round", default=None, metavar="WORKLOAD",
+                    help="time only full rounds (start, fill with in-kernel marks, wait) of a small "
+                         "workload, --steps rounds (for per-kernel traces and counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the P ranks of the "
@@ -500,6 +512,11 @@ def main():
         torch.cuda.synchronize()
         del x, y
         torch.cuda.empty_cache()
+    if args.small_round:
+        r = run_small_round(torch, tc, workloads, BASE_SEED, args.small_round, args.steps,
+                            premark=args.premark)
+        print(json.dumps(dict(workload=args.small_round, rounds=args.steps, **r)), flush=True)
+        return
     h = run_headline(args, torch, tc, workloads, BASE_SEED)
     w = h["w"]
     extras = {}
