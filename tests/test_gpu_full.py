@@ -216,6 +216,64 @@ def test_u32_tiles_shuffled_p8_rounds():
         pair.close()
 
 
+def _random_builder_workload(rng):
+    P = int(rng.integers(2, 6))
+    elem = str(rng.choice(["u8", "bf16", "u32"]))
+    rows, cols = int(rng.integers(5, 48)), int(rng.integers(5, 70))
+    w = dict(P=P, rows=rows, cols=cols, elem=elem, rounds=2)
+    if rng.random() < 0.4:
+        w["stride"] = cols + int(rng.integers(1, 9))
+    b = int(rng.integers(0, 3))
+    if b == 0:
+        w.update(builder="whole", writers=int(rng.integers(1, 4)))
+    elif b == 1:
+        w.update(builder="chunks", n=int(rng.integers(1, min(rows, 6) + 1)), writers=int(rng.integers(1, 4)))
+    else:
+        w.update(builder="tile_chunks", bm=int(rng.integers(4, 20)), bn=int(rng.integers(4, 24)),
+                 tiles_per_chunk=int(rng.integers(1, 5)))
+        if rng.random() < 0.5:
+            w["group_m"] = int(rng.integers(1, 4))
+    return w
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_builders_marked_one_at_a_time(case):
+    # Random views (u8/bf16/u32, padded strides), builders, writer counts and
+    # tile orders; every mark of the round issued on its own, in a seeded
+    # random order across ranks and chunks.  After each mark the gate rows
+    # and queue cursors must equal the oracle's (a gate opens only on its
+    # last writer's mark; arrivals only in schedule order); after each round
+    # the replicas are compared byte for byte.
+    rng = np.random.default_rng(500 + case)
+    w = _random_builder_workload(rng)
+    pair = Pair(w, seed=BASE_SEED + 77 * case, engine_ctas=int(rng.integers(1, 9)))
+    try:
+        for r in (1, 2):
+            h = pair.plan.start(pair.stream)
+            pair.plan.fill(h, pair.tv, pair.seed, kind=w["elem"], mark=False, stream=pair.stream)
+            pair.sim.start()
+            for p in range(pair.P):
+                oracle_produce(pair.sim.rep[p], pair.ov[p], w["elem"], pair.seed, p, r)
+            marks = [(p, c) for p in range(pair.P) for c in range(pair.sim.n[p])
+                     for _ in range(pair.sim.writers(p, c))]
+            marks = [marks[i] for i in rng.permutation(len(marks))]
+            log(f"random builders case {case} round {r}: {w} engine, {len(marks)} single marks")
+            for p, c in marks:
+                pair.plan.mark(h, p, c, 1, stream=pair.stream)
+                pair.sim.mark(p, c)
+                want_g = pair.sim.gate_bytes()
+                ok = wait_until(lambda: np.array_equal(pair.plan.cursors(), pair.sim.cur)
+                                and np.array_equal(pair.plan.gates(), want_g), 5.0)
+                assert ok, f"case {case} round {r} after mark ({p},{c})"
+            pair.plan.wait(10.0)
+            pair.sim.wait()
+            pair.compare(f"random builders case {case} round {r}")
+            pair.plan.next_round()
+            pair.sim.next_round()
+    finally:
+        pair.close()
+
+
 def test_head_of_line_stepped_p8():
     w = workloads.FULL["u32_tiles_shuffled_p8"]
     pair = Pair(w)
