@@ -348,6 +348,27 @@ def test_rank_that_sends_nothing_and_single_rank():
     _run_all_rounds("single rank", w1)
 
 
+def test_plan_where_no_rank_sends():
+    # Every schedule empty: rounds still start, complete and advance, and the
+    # replicas keep their sentinel.
+    w = dict(P=3, rows=8, cols=32, elem="u32", builder="whole", writers=1, rounds=3)
+    pair = Pair(w)
+    try:
+        _swap_in(pair, [None] * 3, [None] * 3)
+        for r in range(1, 4):
+            log(f"no sender round {r}")
+            h = pair.plan.start(pair.stream)
+            pair.plan.fill(h, pair.tv, pair.seed, kind="u32", stream=pair.stream)
+            pair.plan.wait(10.0)
+            assert pair.plan.state == "DONE"
+            oplan.run_round(pair.sim, lambda p, rr: None)
+            pair.compare(f"no sender round {r}")
+            pair.plan.next_round()
+            pair.sim.next_round()
+    finally:
+        pair.close()
+
+
 def test_withheld_mark_times_out_then_resumes():
     w = dict(workloads.SMALL["u32_chunks_ragged_p3"])
     pair = Pair(w)
