@@ -156,6 +156,35 @@ def test_plan_queued_behind_another_is_closing():
         pair.close()
 
 
+def test_nested_plans_in_with_blocks():
+    # Two plans as nested context managers over separate buffers ([TP]
+    # Model: a plan is a context manager; leaving the block closes it).  A
+    # round of each runs inside the inner block, the outer plan runs a second
+    # round after the inner one has closed, and both match their oracles.
+    wa = dict(P=3, rows=24, cols=40, elem="u32", builder="chunks", n=3, writers=2, rounds=2)
+    wb = dict(P=2, rows=16, cols=64, elem="bf16", builder="whole", writers=3, rounds=1)
+    a, b = Pair(wa), Pair(wb, seed=BASE_SEED + 1)
+    a.plan.close()
+    b.plan.close()
+    with tc.TriggeredPlan(a.rep, a.ts, backstop_s=20.0) as pa:
+        a.plan = pa
+        with tc.TriggeredPlan(b.rep, b.ts, backstop_s=20.0) as pb:
+            b.plan = pb
+            for pair, name in ((a, "outer"), (b, "inner")):
+                log(f"nested {name} round 1")
+                pair.gpu_round_fill()
+                pair.oracle_round()
+                pair.compare(f"nested {name} round 1")
+                pair.plan.next_round()
+                pair.sim.next_round()
+        assert pb.close() == "CLOSED"           # already closed by its block
+        log("nested outer round 2")
+        a.gpu_round_fill()
+        a.oracle_round()
+        a.compare("nested outer round 2")
+    assert pa.close() == "CLOSED"
+
+
 def _swap_in(pair, tsched, osched_list, **plan_kw):
     """Replace the Pair's plan and oracle with other schedules on the same buffers."""
     pair.plan.close()
