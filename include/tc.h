@@ -152,7 +152,8 @@ typedef struct tc_plan tc_plan;          /* opaque */
 /* One chunk holding the whole view, completed by `writers` marks (one per
  * program that writes it, marked once each at its end) ([TP] Model: whole()).
  * Out: *out, freed with tc_schedule_free.  TC_EINVAL on a zero-size view,
- * row_stride < cols, or writers == 0. */
+ * row_stride < cols, a view whose last byte lies at 2^62 or beyond (every
+ * builder checks its view so), or writers == 0. */
 int tc_schedule_whole(const tc_view* view, uint32_t writers, tc_schedule** out);
 
 /* n chunks, one per row block, completed in order ([TP] Model: chunks()).
@@ -175,7 +176,8 @@ int tc_schedule_tile_chunks(const tc_view* view, uint32_t bm, uint32_t bn,
  * must cover regions[first_region .. first_region+num_regions) back to back
  * in order; regions are normalised and cut at 1 GiB like the builders'.
  * nchunks == 0 gives the empty schedule of a rank that sends nothing
- * ([TP] Requirements and limits).  TC_EINVAL on a malformed table. */
+ * ([TP] Requirements and limits).  TC_EINVAL on a malformed table or a
+ * region whose last byte lies at 2^62 or beyond. */
 int tc_schedule_from_arrays(const tc_chunk* chunks, uint32_t nchunks,
                             const tc_region* regions, uint32_t nregions, tc_schedule** out);
 

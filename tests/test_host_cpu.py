@@ -144,6 +144,15 @@ def test_builder_errors():
         tc.whole(tc.View(0, 0, 4, 4, 4, 0))
     with pytest.raises(tc.InvalidArgument):
         tc.whole(tc.View(0, 4, 4, 3, 4, 0))
+    # extents whose byte arithmetic would wrap 64 bits are refused, not wrapped
+    with pytest.raises(tc.InvalidArgument):
+        tc.whole(tc.View(0, 1 << 40, 4, 1 << 40, 4, 0))
+    with pytest.raises(tc.InvalidArgument):
+        tc.chunks(tc.View((1 << 63) + 16, 4, 4, 4, 4, 0), 2)
+    with pytest.raises(tc.InvalidArgument):
+        tc.from_arrays([(0, 1, 1)], [(0, 1 << 40, 16, 1 << 40)])
+    with pytest.raises(tc.InvalidArgument):
+        tc.from_arrays([(0, 1, 1)], [((1 << 64) - 64, 1, 128, 128)])
 
 
 def test_order_grouped_matches_oracle():

@@ -56,11 +56,29 @@ void push_region(uint64_t off, uint64_t rows, uint64_t row_bytes, uint64_t pitch
 
 using tc::fail;
 
+// One past the last byte of `rows` rows of `row_bytes` at `pitch` from
+// `off`, or false when that does not fit in 62 bits (no buffer is that big,
+// and no address computed from it can wrap).
+static bool extent_end(uint64_t off, uint64_t rows, uint64_t row_bytes, uint64_t pitch,
+                       uint64_t* end) {
+  uint64_t span = 0, e = 0;
+  if (__builtin_mul_overflow(rows - 1, pitch, &span) || __builtin_add_overflow(span, row_bytes, &e) ||
+      __builtin_add_overflow(e, off, &e) || e >= (1ull << 62))
+    return false;
+  *end = e;
+  return true;
+}
+
 static int check_view(const tc_view* v) {
   if (!v) return fail(TC_EINVAL, "view is NULL");
   if (v->rows == 0 || v->cols == 0 || v->elem_bytes == 0)
     return fail(TC_EINVAL, "view has a zero size");
   if (v->row_stride < v->cols) return fail(TC_EINVAL, "row_stride < cols");
+  uint64_t pitch = 0, row_bytes = 0, end = 0;
+  if (__builtin_mul_overflow(v->row_stride, (uint64_t)v->elem_bytes, &pitch) ||
+      __builtin_mul_overflow(v->cols, (uint64_t)v->elem_bytes, &row_bytes) ||
+      !extent_end(v->byte_offset, v->rows, row_bytes, pitch, &end))
+    return fail(TC_EINVAL, "view spans more than 2^62 bytes");
   return TC_OK;
 }
 
@@ -172,9 +190,14 @@ int tc_schedule_from_arrays(const tc_chunk* chunks, uint32_t nchunks, const tc_r
     const size_t first = s->regions.size();
     for (uint32_t i = c.first_region; i < c.first_region + c.num_regions; ++i) {
       const tc_region& r = regions[i];
+      uint64_t end = 0;
       if (r.rows == 0 || r.row_bytes == 0 || (r.rows > 1 && r.pitch < r.row_bytes)) {
         delete s;
         return fail(TC_EINVAL, "from_arrays: region with zero size or pitch < row_bytes");
+      }
+      if (!extent_end(r.offset, r.rows, r.row_bytes, r.rows > 1 ? r.pitch : 0, &end)) {
+        delete s;
+        return fail(TC_EINVAL, "from_arrays: region spans more than 2^62 bytes");
       }
       tc::push_region(r.offset, r.rows, r.row_bytes, r.pitch, s->regions);
     }
