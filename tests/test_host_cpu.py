@@ -228,3 +228,13 @@ def test_workspace_bytes():
     out = C.c_uint64()
     assert tc.lib().tc_plan_workspace_bytes(2, ptrs, 0, C.byref(out)) == 0
     assert out.value >= 2 * 4 * 64 and out.value % 256 == 0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # The P ranks are simulated on one GPU: --gpus N > 1 exits with a message.
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
