@@ -32,9 +32,15 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
 
-ENGINE_SOURCES = ("include/tc_device.h", "triggered_copy_amd/csrc/internal.h",
-                  "triggered_copy_amd/csrc/plan_internal.h", "triggered_copy_amd/csrc/plan.hip",
-                  "triggered_copy_amd/csrc/schedule.cpp")
+# The code that decides the copy engine's traffic for a given schedule: the
+# shared headers, plan.hip's device code and launch (everything before its
+# host API, which starts at `using namespace tc;`), and the piece builder of
+# schedule.cpp.  (file, first line containing, line after the end containing)
+ENGINE_SOURCES = (("include/tc_device.h", None, None),
+                  ("triggered_copy_amd/csrc/internal.h", None, None),
+                  ("triggered_copy_amd/csrc/plan_internal.h", None, None),
+                  ("triggered_copy_amd/csrc/plan.hip", None, "using namespace tc;"),
+                  ("triggered_copy_amd/csrc/schedule.cpp", "void tc::build_pieces(", None))
 TRAFFIC_PROFILE = "profiles/engine_kernel_u32_chunks_1p5g_p4_hbm_bytes.md"
 
 
@@ -51,26 +57,38 @@ def code_only(src):
     return " ".join(src.split())
 
 
+def engine_source_hash():
+    """sha256 over the code (comments and whitespace removed) of the parts of
+    ENGINE_SOURCES, in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f, start, end in ENGINE_SOURCES:
+        with open(os.path.join(ROOT, f)) as fh:
+            text = fh.read()
+        if start is not None:
+            text = text[text.index(start):]
+        if end is not None:
+            text = text[:text.index(end)]
+        h.update(code_only(text).encode())
+    return h.hexdigest()
+
+
 def counted_traffic(workload, engine_ctas, piece_bytes):
     """HBM bytes per engine launch from the committed FETCH_SIZE/WRITE_SIZE
     summary, or None when the engine sources or the launch differ from the
     ones the counters were taken on."""
-    import hashlib
     import re
     path = os.path.join(ROOT, TRAFFIC_PROFILE)
     if workload != "u32_chunks_1p5g_p4" or engine_ctas != 1024 or piece_bytes != 8192:
         return None
     try:
         text = open(path).read()
-        h = hashlib.sha256()
-        for f in ENGINE_SOURCES:
-            with open(os.path.join(ROOT, f)) as fh:
-                h.update(code_only(fh.read()).encode())
-    except OSError:
+        digest = engine_source_hash()
+    except (OSError, ValueError):
         return None
     want = re.search(r"engine_source_sha256: ([0-9a-f]{64})", text)
     val = re.search(r"traffic_bytes_per_launch: (\d+)", text)
-    if not want or not val or want.group(1) != h.hexdigest():
+    if not want or not val or want.group(1) != digest:
         return None
     return int(val.group(1))
 
