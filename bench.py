@@ -480,6 +480,38 @@ def cpu_baseline(workloads, seed, budget_s=12.0):
                       f"(produce + marks + in-order copies + wait) in {dt * n:.1f} s on one core"}
 
 
+def cpu_copy_baseline(workloads, sample_bytes=256 << 20, reps=5):
+    """One GPU's share of the headline round done by host cores with
+    numpy.copyto: a source block copied into P - 1 destinations, on one core
+    and on every core the process may use (threads over slices).  A bounded
+    sample of the 1.5 GiB block; reported as delivered GB/s.  Context only."""
+    import concurrent.futures
+    import numpy as np
+    w = workloads.FULL["u32_chunks_1p5g_p4"]
+    P = w["P"]
+    src = np.frombuffer(np.random.default_rng(1).bytes(sample_bytes), dtype=np.uint8)
+    dst = [np.empty(sample_bytes, dtype=np.uint8) for _ in range(P - 1)]
+    cores = len(os.sched_getaffinity(0))
+
+    def one(lo, hi):
+        for d in dst:
+            np.copyto(d[lo:hi], src[lo:hi])
+
+    def timed(nthreads):
+        step = -(-sample_bytes // nthreads)
+        best = float("inf")
+        with concurrent.futures.ThreadPoolExecutor(max_workers=nthreads) as ex:
+            for _ in range(reps):
+                t0 = time.perf_counter()
+                list(ex.map(lambda i: one(i * step, min(sample_bytes, (i + 1) * step)), range(nthreads)))
+                best = min(best, time.perf_counter() - t0)
+        return (P - 1) * sample_bytes / best / 1e9
+
+    return {"unit": "GB/s", "one_core": round(timed(1), 2), "all_cores": round(timed(cores), 2),
+            "cores": cores, "kind": "numpy.copyto",
+            "sample": f"{sample_bytes >> 20} MiB source copied to {P - 1} destinations, best of {reps}"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -579,6 +611,8 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline: the oracle on a bounded sample")
         cpu = cpu_baseline(workloads, BASE_SEED)
+        log("cpu copy baseline: numpy.copyto of one GPU's share, sampled")
+        extras["cpu_copy_baseline"] = cpu_copy_baseline(workloads)
     line = {
         "metric": METRIC,
         "value": round(h["value"], 2),
