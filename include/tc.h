@@ -230,7 +230,7 @@ int tc_plan_validate(const tc_plan_desc* desc);
 /* Creates a plan ([TP] Model: TriggeredPlan(ctx, out, schedule), with the
  * schedule-per-rank form of [PR] API).  Validates, lays out and zeroes the
  * workspace (gates start at zero), uploads the descriptors once (region sizes
- * are fixed at creation, [TP] contract item 4), and creates the copy-engine
+ * are fixed at creation, [TP] The kernel author's contract), and creates the copy-engine
  * stream.  Round = 1, state READY.  The engine stream always has a hardware
  * queue of its own (it is created CU-masked: with cu_mask, or with every CU),
  * because the engine runs before the producer it waits for and streams that
@@ -273,7 +273,8 @@ int tc_plan_handle(const tc_plan* plan, tc_handle* out);
  *   TC_ESTATE   not STARTED. */
 int tc_plan_wait(tc_plan* plan, uint64_t timeout_us);
 
-/* Declares this round's data consumed ([TP] contract item 6).  DONE -> READY,
+/* Declares this round's data consumed ([TP] The kernel author's contract: next_round()
+ * means done reading this round's data).  DONE -> READY,
  * round + 1.  TC_ESTATE unless DONE; TC_EROUNDS at round 2^32 - 1. */
 int tc_plan_next_round(tc_plan* plan);
 

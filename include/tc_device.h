@@ -11,7 +11,8 @@
  * Nobody needs to learn that it was the last writer, so the increment does
  * not wait for its result.
  *
- * Consumer side (same section; [TP] The kernel author's contract, item 5):
+ * Consumer side (same section; [TP] The kernel author's contract: arrived
+ * and wait are called uniformly across the CTA):
  * arrived/wait read the arrival counter, then acquire at system scope.  One
  * wave reads, the CTA barrier hands the result to every wave, and polling
  * loops count polls instead of reading a clock, so every wave takes the same
