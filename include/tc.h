@@ -38,11 +38,11 @@ extern "C" {
 #define TC_MAX_RANKS 16
 #define TC_GATE_ROW_BYTES 64
 /* A linear region moves at most 1 GiB; longer ranges are cut by the builders
- * ([TP] Model; Requirements and limits: the linear copy packet's byte count
- * is a 30-bit field). */
+ * ([TP] Model; Requirements and limits: the DMA packet that copies a byte
+ * range holds its length in 30 bits). */
 #define TC_LINEAR_MAX_BYTES (1ull << 30)
-/* Rounds start at 1 and gates are never reset, so a plan allows 2^32 - 1
- * rounds ([TP] Gates and rounds). */
+/* The first round is 1 and no gate is ever cleared, so one plan runs at most
+ * 2^32 - 1 rounds ([TP] Gates and rounds). */
 #define TC_ROUND_LIMIT 0xFFFFFFFFu
 
 enum tc_status {
@@ -96,8 +96,8 @@ typedef struct tc_region {
   uint64_t pitch;
 } tc_region;
 
-/* An ordered group of regions sent together with one arrival per peer, and
- * the number of mark_ready calls that complete it each round ([TP] Model). */
+/* Regions delivered as one unit, in their order, with a single arrival per
+ * peer, plus how many mark_ready calls finish it in a round ([TP] Model). */
 typedef struct tc_chunk {
   uint32_t first_region;
   uint32_t num_regions;
@@ -105,8 +105,8 @@ typedef struct tc_chunk {
   uint32_t rsvd;
 } tc_chunk;
 
-/* A 64-byte gate row ([TP] Gates and rounds: ready, arrival and a writer
- * counter; the copy side polls the gate against the round with >=).  As
+/* A 64-byte gate row ([TP] Gates and rounds: the fields ready, arrival and
+ * the marks' count; the copy side opens on ready >= round).  As
  * reported by tc_plan_read_gates: in rank p's own table the row of its chunk
  * c holds ready (= the last round whose gate opened) and writers (cumulative
  * marks); in a peer q's table the same row holds arrival (= rounds delivered
@@ -223,8 +223,8 @@ int tc_plan_workspace_bytes(uint32_t nranks, const tc_schedule* const* schedules
                             uint64_t piece_bytes, uint64_t* out_bytes);
 
 /* The creation checks alone, on the host, with no GPU: region bounds, own
- * rows, cross-rank overlap ([TP] Requirements and limits: two ranks may not
- * send the same bytes; one rank may repeat its own), writers > 0. */
+ * rows, cross-rank overlap ([TP] Requirements and limits: no byte may come
+ * from two different ranks; a rank may list its own bytes twice), writers > 0. */
 int tc_plan_validate(const tc_plan_desc* desc);
 
 /* Creates a plan ([TP] Model: TriggeredPlan(ctx, out, schedule), with the
@@ -246,9 +246,11 @@ int tc_plan_validate(const tc_plan_desc* desc);
 int tc_plan_create(const tc_plan_desc* desc, tc_plan** out);
 
 /* Starts the round ([TP] Model: start()).  READY -> STARTED.  The copy
- * engine is launched on the plan's stream after all work already queued on
- * `stream` (so work queued before the call is covered, [TP] contract item
- * 6), and *out receives the handle for producer and consumer kernels.
+ * engine is launched on the plan's stream behind all work already queued on
+ * `stream`, so reads of the previous round's data issued before start() are
+ * not overwritten ([TP] The kernel author's contract: copies may overwrite a
+ * peer's buffer once it has moved on to the next round); *out receives the
+ * handle for producer and consumer kernels.
  * `stream` is the producer's stream; it may not be the legacy default stream
  * (NULL), which waits for every blocking stream and so for the engine.
  * Between start() and the launch of the producer nothing may wait for the
@@ -273,15 +275,15 @@ int tc_plan_handle(const tc_plan* plan, tc_handle* out);
  *   TC_ESTATE   not STARTED. */
 int tc_plan_wait(tc_plan* plan, uint64_t timeout_us);
 
-/* Declares this round's data consumed ([TP] The kernel author's contract: next_round()
- * means done reading this round's data).  DONE -> READY,
+/* Tells the plan this round's data has been read ([TP] The kernel author's
+ * contract: after next_round() peers may overwrite it).  DONE -> READY,
  * round + 1.  TC_ESTATE unless DONE; TC_EROUNDS at round 2^32 - 1. */
 int tc_plan_next_round(tc_plan* plan);
 
 /* Closes the plan ([TP] Model: close / leaving the with block; The kernel
  * author's contract: closing mid-round).  Safe in any state.  In the middle
- * of a round every gate of the plan is forced open, so the copy engine sends
- * each rank's chunks as they stand (after a timeout it is run again for
+ * of a round every gate of the plan is forced open, so the copy engine
+ * delivers every chunk with whatever bytes it holds at that moment (after a timeout it is run again for
  * that); then its streams, events and host words are freed.  The caller's
  * buffers keep what was delivered.  Plans with the same CU mask share one
  * engine stream, so their rounds run in start() order; a plan whose engine
@@ -386,7 +388,7 @@ int tc_mark(tc_plan* plan, const tc_handle* h, uint32_t rank, uint32_t chunk,
 /* Persistent bf16 GEMM producer ([TP] Model, the tiled-kernel example):
  * C[M,N] = A[M,K] * B with B given as Bt[N,K] (K contiguous), bf16 in, fp32
  * accumulate, bf16 out (round to nearest even), C row stride ldc elements.
- * 128x128 tiles; program p takes steps p, p + programs, ...; step s computes
+ * 128x128 tiles; program p handles the steps s with s % programs == p; step s computes
  * tile tc_tile_of(s, tm, tn, group_m) and, when h != NULL, then marks chunk
  * first_chunk + s / tiles_per_chunk of rank `rank`.  When programs is a
  * multiple of 8, consecutive programs run on one XCD (workgroups are dealt

@@ -11,8 +11,8 @@
  * Nobody needs to learn that it was the last writer, so the increment does
  * not wait for its result.
  *
- * Consumer side (same section; [TP] The kernel author's contract: arrived
- * and wait are called uniformly across the CTA):
+ * Consumer side (same section; [TP] The kernel author's contract: every wave
+ * of the CTA makes the same arrived/wait calls):
  * arrived/wait read the arrival counter, then acquire at system scope.  One
  * wave reads, the CTA barrier hands the result to every wave, and polling
  * loops count polls instead of reading a clock, so every wave takes the same
@@ -93,7 +93,7 @@ __device__ inline uint64_t* tc_mark_stripe(const tc_handle& h, uint32_t src, uin
  * the closing barrier, so it cannot be merged into a caller's loop back-edge. */
 template <bool kWriteBack>
 __device__ inline void tc_mark_ready_impl(const tc_handle& h, uint32_t rank, uint32_t chunk) {
-  __builtin_amdgcn_s_waitcnt(TC_WAITCNT_VMCNT0);  // this wave's stores are done
+  __builtin_amdgcn_s_waitcnt(TC_WAITCNT_VMCNT0);  // wait for this wave's own stores
   __syncthreads();                                // ... and so are every other wave's
   if (tc_is_cta_leader()) {
     uint64_t* stripe = tc_mark_stripe(h, rank, chunk, blockIdx.x % TC_MARK_STRIPES);

@@ -12,8 +12,9 @@ Reading for P simulated ranks on one device: the P windows are stacked as
 ``W[P, P]`` int32, ``W[q, s]`` = the cell of row s in rank q's window, written
 only by rank s.
 
-The data reveal of the same page (a rank stages its slice, barriers, then
-reads the next rank's slice; the golden result is y[r] = x[(r + 1) % N]) is
+The data reveal of the same page (each rank writes its own slot, all pass
+the barrier, each then picks up its right-hand neighbour's slot, so that
+y[r] = x[(r + 1) % N]) is
 kept with a double-buffered stage ``x[g % 2][m]`` so that generations can
 follow each other without a second barrier.
 """

@@ -3,11 +3,12 @@
 What is simulated, after "Triggered Plans":
 
 * *Model*: a round is ``start()``, every chunk marked ready by its writers,
-  ``wait()``; the plan is prepared once and reused every round.
-* *Gates and rounds*: each chunk has a 64-byte gate row holding ``ready``,
-  ``arrival`` and a writer counter; the copy side polls the low 32 bits of
-  ``ready`` with ``>=``; rounds start at 1, add 1 per ``next_round()``, gates
-  are never reset, so a plan allows 2**32 - 1 rounds.
+  ``wait()``; one plan serves every round, set up once.
+* *Gates and rounds*: a chunk's 64-byte gate row carries ``ready``,
+  ``arrival`` and the count of writers' marks; the copy side compares the
+  lower half of ``ready`` with the round using ``>=``; the first round is 1,
+  each ``next_round()`` adds 1 and nothing ever clears a gate, hence at most
+  2**32 - 1 rounds per plan.
 * *Memory ordering*: the writer counter is incremented once per mark; the
   writer whose increment completes the round's count opens the gate by
   writing the round number into ``ready``.
@@ -15,9 +16,9 @@ What is simulated, after "Triggered Plans":
   notes*: per peer, one queue that runs, in prepared order, for each chunk:
   poll ``ready >= round``, copy every region, add 1 to the chunk's arrival
   counter on that peer.
-* *The kernel author's contract*: queues run strictly in order (a chunk
-  completed early waits for the ones before it); ``wait()`` raises on extra
-  marks and a timeout names the chunks still short.
+* *The kernel author's contract*: a queue keeps its prepared order (a chunk
+  that finishes early still waits behind those listed before it); ``wait()`` raises on extra
+  marks, and a timeout reports which chunks are still missing marks or copies.
 
 Readings (where the pages are silent):
 

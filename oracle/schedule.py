@@ -1,14 +1,15 @@
 """Regions, chunks and schedules (oracle side).
 
-Follows "Triggered Plans", section *Model*: a *region* is one copy, a byte
-range or a 2-D sub-window of a strided tensor, landing at the same offset in
-every peer's buffer; a *chunk* is an ordered group of regions with a number
-of *writers*; a *schedule* lists one rank's chunks in completion order.  The
+Follows "Triggered Plans", section *Model*: a *region* is the unit of one
+copy (bytes back to back, or a 2-D window of a strided tensor) and lands at
+the identical offset in every peer's buffer; a *chunk* bundles regions, in order,
+under one writers count; a *schedule* is one rank's list of chunks in the
+order its producer finishes them.  The
 builders ``whole``, ``chunks`` and ``tile_chunks`` and the 1 GiB split of
 linear copies come from the same section and from *Requirements and limits*.
 Validation follows *The kernel author's contract* (a failed create keeps
-nothing) and *Requirements and limits* (two ranks may not send the same
-bytes); the own-rows check is the all-gather wrapper's, described at the end
+nothing) and *Requirements and limits* (no byte may be sent by two
+different ranks); the own-rows check is the all-gather wrapper's, described at the end
 of *Model*.
 
 Readings where the pages are silent (each listed in the design notes):

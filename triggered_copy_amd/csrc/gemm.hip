@@ -1,8 +1,8 @@
 // Persistent bf16 GEMM producer with an in-kernel mark_ready.
 //
 // [TP] = "Triggered Plans" (Iris documentation), section Model: the example
-// producer is a persistent tiled kernel whose program p takes steps p,
-// p + programs, ...; each step computes the tile tile_of(step) picks, stores
+// producer is a persistent tiled kernel: program p handles the steps
+// congruent to p modulo the number of programs; each step computes the tile tile_of(step) picks, stores
 // it, then marks chunk first_chunk + step / tiles_per_chunk ready.  The host
 // builds the schedule with tile_chunks() from the same tile_of, so the two
 // cannot disagree.

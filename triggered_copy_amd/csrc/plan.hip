@@ -27,8 +27,8 @@
 //  * Every wave counts its finished piece without waiting for the atomic's
 //    result; the wave holding a chunk's last piece waits for the others'
 //    counts, then until every earlier chunk of the same source has been
-//    signalled (head-of-line order, [TP] The kernel author's contract: chunks
-//    complete in schedule order), then stores the
+//    signalled (head-of-line order, [TP] The kernel author's contract: a
+//    queue delivers a source's chunks in schedule order), then stores the
 //    round into `arrival` in every receiver's gate row and advances the
 //    queue cursors.
 //  * All control flow is wave-uniform; lanes past the end of a piece are

@@ -2,7 +2,7 @@
 //
 // [TP] = "Triggered Plans" (Iris documentation).  Producers write their part
 // of the output and mark each chunk ready once per writer (section Model;
-// The kernel author's contract: exactly writers marks per round); mark_ready is the device function of
+// The kernel author's contract: one mark per writer per round); mark_ready is the device function of
 // section Memory ordering.  The consumer reads a chunk only after
 // arrived/wait (section Memory ordering, consumer side).
 //
