@@ -160,6 +160,8 @@ def run_headline(args, torch, tc, workloads, seed):
     out = dict(ms_per_step=ms_per_step, value=delivered / (ms_per_step * 1e-3) / 1e9,
                engine_ms_mean=eng, engine_ms_median=statistics.median(engine_ms),
                engine_ms_min=min(engine_ms), achieved=achieved,
+               engine_ms_p10=sorted(engine_ms)[len(engine_ms) // 10],
+               engine_ms_p90=sorted(engine_ms)[(9 * len(engine_ms)) // 10],
                window_ms_median=statistics.median(window_ticks) / 1e5,
                engine_ctas=st["engine_ctas"], pieces=st["pieces"],
                piece_bytes=args.piece_bytes or 8192,
@@ -634,7 +636,10 @@ def main():
                      "unit": "GB/s", "frac": round(h["achieved"] / HBM_PEAK_GBS, 4),
                      "traffic": counted_traffic(args.workload, h["engine_ctas"], h["piece_bytes"]),
                      "kernel": "engine_kernel", "algo_bytes_per_launch": h["algo_bytes"],
-                     "launch_ms_mean": round(h["engine_ms_mean"], 4)},
+                     "launch_ms_mean": round(h["engine_ms_mean"], 4),
+                     "launch_ms_median": round(h["engine_ms_median"], 4),
+                     "launch_ms_p10": round(h["engine_ms_p10"], 4),
+                     "launch_ms_p90": round(h["engine_ms_p90"], 4)},
         "hbm_frac": round(h["achieved"] / HBM_PEAK_GBS, 4),
         "engine_window_ms_median": round(h["window_ms_median"], 4),
         "overlap_slowdown_pct": (round(extras["gemm_overlap"]["slowdown_pct"], 2)
