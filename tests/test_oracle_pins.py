@@ -385,6 +385,36 @@ def test_interleavings_are_confluent():
         assert state == ref
 
 
+def test_counters_only_mode_follows_the_full_simulation():
+    # The counters-only mode (no replica bytes; used for the 1.5 GiB GPU
+    # runs) is tied to the pinned full simulation: on random schedules and
+    # mark orders, over several rounds, its gate rows, cursors and delivery
+    # logs equal the full mode's after every single mark.
+    rnd = random.Random(11)
+    for trial in range(40):
+        P = rnd.randint(2, 4)
+        rows, cols = rnd.randint(4, 12), rnd.randint(3, 9)
+        nbytes = P * rows * cols * 4
+        views = [schedule.View(p * rows * cols * 4, rows, cols, cols, 4) for p in range(P)]
+        sched = [schedule.chunks(v, rnd.randint(1, min(rows, 4)), rnd.randint(1, 3)) for v in views]
+        full = plan.PlanSim([np.zeros(nbytes, np.uint8) for _ in range(P)], sched)
+        bare = plan.PlanSim(None, sched, buffer_bytes=nbytes)
+        for r in range(1, 4):
+            full.start()
+            bare.start()
+            marks = [(p, c) for p in range(P) for c in range(full.n[p]) for _ in range(full.writers(p, c))]
+            rnd.shuffle(marks)
+            for p, c in marks:
+                full.mark(p, c)
+                bare.mark(p, c)
+                assert np.array_equal(full.gates, bare.gates) and np.array_equal(full.cur, bare.cur)
+            full.wait()
+            bare.wait()
+            assert full.log == bare.log
+            full.next_round()
+            bare.next_round()
+
+
 def test_simulation_equals_plain_definition():
     rnd = random.Random(5)
     for P in (2, 3, 4):
