@@ -594,6 +594,43 @@ def test_barrier_missing_peer_ends_with_status():
     assert int(status.item()) != 0
 
 
+def test_consumer_wait_runs_out_of_polls():
+    # A chunk whose last mark is withheld never arrives: the consumer's wait
+    # for it ends after its poll budget with status 2 (the kernel exits), the
+    # other chunks are consumed with status 1; closing the plan then sends the
+    # withheld chunk as it stands.
+    w = dict(workloads.SMALL["u32_tiles_shuffled_p3"])
+    pair = Pair(w)
+    try:
+        G = pair.plan.G
+        out = torch.full_like(pair.rep[0], 0x5A)
+        status = torch.zeros(G, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        h = pair.plan.start(pair.stream)
+        pair.plan.fill(h, pair.tv, pair.seed, kind="u32", mark=False, stream=pair.stream)
+        last = pair.sim.n[0] - 1
+        for p in range(pair.P):
+            for c in range(pair.sim.n[p]):
+                wr = pair.sim.writers(p, c)
+                n = wr - 1 if (p, c) == (0, last) else wr
+                if n:
+                    pair.plan.mark(h, p, c, n, stream=pair.stream)
+        log("consumer with a withheld chunk, 2000 polls per wait")
+        pair.plan.consume_copy(h, 2, out, status, max_polls=2000, stream=pair.stream)
+        # Read on the producers' stream: a copy on the legacy default stream
+        # would wait for the engine, which waits for the withheld gate.
+        with torch.cuda.stream(pair.stream):
+            st = status.cpu().numpy()
+        g_withheld = last                      # rank 0's chunks come first
+        assert st[g_withheld] == 2, st.tolist()
+        assert (np.delete(st, g_withheld) == 1).all(), st.tolist()
+        with pytest.raises(tc.PlanTimeout):
+            pair.plan.wait(0.2)
+        assert pair.plan.close() == "CLOSED"
+    finally:
+        pair.close()
+
+
 def test_device_view_consumer_sees_fresh_data():
     w = dict(workloads.SMALL["u32_tiles_shuffled_p3"])
     pair = Pair(w)
