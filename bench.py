@@ -122,10 +122,11 @@ def run_headline(args, torch, tc, workloads, seed):
     plan = tc.TriggeredPlan(rep, scheds, engine_ctas=args.engine_ctas, piece_bytes=args.piece_bytes)
     prod = torch.cuda.Stream()
     engine_ms, window_ticks = [], []
+    fill_kw = {args.fill: True}
 
     def step(record):
         h = plan.current_handle()
-        plan.fill(h, views, seed, kind=w["elem"], mark=False, waves=True, stream=prod)
+        plan.fill(h, views, seed, kind=w["elem"], mark=False, stream=prod, **fill_kw)
         if args.premark:
             # Profiling order: the marks precede start(), so no kernel ever
             # waits on a kernel queued after it (a profiler that runs kernels
@@ -168,15 +169,15 @@ def run_headline(args, torch, tc, workloads, seed):
                delivered=delivered, algo_bytes=algo_bytes, S=S, P=P, w=w)
 
     # Full triggered rounds: the fill marks each chunk as its writers finish,
-    # so copies overlap the production of later chunks.  The producer is a
-    # persistent grid completing every rank's chunk 0 first, then chunk 1, ...
+    # so copies overlap the production of later chunks.  Either producer grid
+    # completes every rank's chunk 0 first, then chunk 1, ...
     if not args.no_extras:
         times = []
         for i in range(max(3, args.steps // 4)):
             torch.cuda.synchronize()
             a = time.perf_counter()
             h = plan.start(prod)
-            plan.fill(h, views, seed, kind=w["elem"], mark=True, waves=True, stream=prod)
+            plan.fill(h, views, seed, kind=w["elem"], mark=True, stream=prod, **fill_kw)
             plan.wait(60.0)
             plan.next_round()
             times.append(time.perf_counter() - a)
@@ -530,6 +531,8 @@ def main():
                     help="also measure the copy engine on N fresh allocations of the replicas")
     ap.add_argument("--gemm-only", action="store_true",
                     help="time only the 4 GEMM producers, with no plan (for counter collection)")
+    ap.add_argument("--fill", choices=("waves", "oneshot"), default="oneshot",
+                    help="producer grid of the headline step: persistent writers or one CTA per 16 KiB block")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--premark", action="store_true",
                     help="issue the marks before start() (for counter collection)")
@@ -630,7 +633,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "P": w["P"], "bytes_per_rank": h["S"],
                    "builder": w["builder"], "chunks": w.get("n", 1), "writers": w["writers"],
-                   "marks": "deferred (fill, start, mark kernel)",
+                   "marks": "deferred (fill, start, mark kernel)", "fill": args.fill,
                    "engine_ctas": h["engine_ctas"], "pieces_per_round": h["pieces"]},
         "roofline": {"bound": "hbm", "achieved": round(h["achieved"], 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(h["achieved"] / HBM_PEAK_GBS, 4),

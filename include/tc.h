@@ -351,15 +351,20 @@ enum { TC_MARK_INKERNEL = 0, TC_MARK_NONE = 1 };
  *             ...; CTA i takes slots i, i + ctas, ...  Chunks complete a few
  *             at a time, so the copy engine can deliver early chunks while
  *             later ones are still produced ([TP] Model: a schedule lists
- *             chunks in the order the producer completes them). */
-enum { TC_FILL_PARALLEL = 0, TC_FILL_SERIAL = 1, TC_FILL_WAVES = 2 };
+ *             chunks in the order the producer completes them).
+ *   ONESHOT:  one CTA per 16 KiB block of every writer's share, blocks in
+ *             the WAVES order, stores written through to memory; the last
+ *             block of a share to finish issues that writer's mark.  Only
+ *             for plans whose every chunk is one byte range and for
+ *             contiguous views (else TC_EINVAL). */
+enum { TC_FILL_PARALLEL = 0, TC_FILL_SERIAL = 1, TC_FILL_WAVES = 2, TC_FILL_ONESHOT = 3 };
 
 typedef struct tc_fill_desc {
   const tc_view* views;   /* host array of P views: rank p's part of the buffer */
   uint64_t seed;
   uint32_t kind;          /* TC_FILL_* ; elem_bytes of the views must match */
   uint32_t mark_mode;     /* TC_MARK_* */
-  uint32_t mode;          /* TC_FILL_PARALLEL / TC_FILL_SERIAL / TC_FILL_WAVES */
+  uint32_t mode;          /* TC_FILL_PARALLEL / SERIAL / WAVES / ONESHOT */
   uint32_t rsvd;
   const uint32_t* order;  /* device, [P][max_chunks] when SERIAL; NULL = schedule order */
   uint32_t order_stride;  /* entries per rank in order[], at least a rank's chunk count */

@@ -179,16 +179,19 @@ def _sample_check(pair, w, r, rng, nsamp=1 << 18):
         assert bad.size == 0, f"rank {p} in replica {q}: {bad.size} sampled elements differ, e.g. index {idx[bad[:4]]}"
 
 
+@pytest.mark.parametrize("oneshot", [False, True], ids=["writer_ctas", "oneshot"])
 @pytest.mark.parametrize("name", ["u32_chunks_1p5g_p4", "u32_whole_1p5g_p4"])
-def test_u32_1p5g_p4_full(name):
+def test_u32_1p5g_p4_full(name, oneshot):
+    # Writer CTAs (one per writer slot) or the one-shot grid (one CTA per
+    # 16 KiB block, the share's last block marking), at the full size.
     w = workloads.FULL[name]
     rng = np.random.default_rng(5)
     pair = Pair(w, oracle_bytes=False)
     try:
         for r in range(1, w["rounds"] + 1):
             deferred = r == 2
-            log(f"{name} round {r} ({'deferred' if deferred else 'in-kernel'} marks)")
-            pair.gpu_round_fill(mark=not deferred, timeout=30.0)
+            log(f"{name} round {r} ({'deferred' if deferred else 'in-kernel'} marks, oneshot={oneshot})")
+            pair.gpu_round_fill(mark=not deferred, timeout=30.0, oneshot=oneshot)
             pair.oracle_round()
             pair.compare(f"{name} round {r}")
             _sample_check(pair, w, r, rng)

@@ -85,6 +85,71 @@ def test_waves_fill():
             pair.close()
 
 
+ONESHOT_CASES = {
+    # blocks per share from one to several, ragged tails
+    "u32_chunks_ragged_p3": dict(workloads.SMALL["u32_chunks_ragged_p3"]),
+    "u32_chunks_multi_block_p4": dict(P=4, rows=300, cols=1000, elem="u32", builder="chunks", n=3,
+                                      writers=5),
+    "u32_whole_p5": dict(workloads.SMALL["u32_whole_p5"]),
+    # shares that start and end off 16-byte boundaries: the byte path
+    "u8_chunks_unaligned_p3": dict(P=3, rows=301, cols=101, elem="u8", builder="chunks", n=4,
+                                   writers=3),
+    "bf16_whole_odd_p2": dict(P=2, rows=7, cols=4097, elem="bf16", builder="whole", writers=7),
+    # more writers than pieces: empty shares still mark
+    "u32_whole_many_writers_p2": dict(P=2, rows=1, cols=3000, elem="u32", builder="whole",
+                                      writers=9),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ONESHOT_CASES))
+def test_oneshot_fill(name):
+    # One CTA per 16 KiB block of each writer's share; the share's last
+    # block to finish marks.  Rounds alternate in-kernel and deferred marks,
+    # so a deferred round must leave the block counters as it found them.
+    w = ONESHOT_CASES[name]
+    pair = Pair(w, piece_bytes=4096)
+    try:
+        for r, mark in ((1, True), (2, False), (3, True), (4, True)):
+            log(f"oneshot {name} round {r} mark={mark}")
+            pair.gpu_round_fill(mark=mark, oneshot=True)
+            pair.oracle_round()
+            pair.compare(f"oneshot {name} round {r}")
+            pair.plan.next_round()
+            pair.sim.next_round()
+    finally:
+        pair.close()
+
+
+def test_oneshot_fill_rejects_tiles_and_strided_views():
+    for name in ("bf16_tiles_ragged_p4", "u8_tiles_odd_p2"):
+        pair = Pair(dict(workloads.SMALL[name]))
+        try:
+            h = pair.plan.start(pair.stream)
+            with pytest.raises(tc.InvalidArgument, match="one byte range"):
+                pair.plan.fill(h, pair.tv, pair.seed, kind=pair.w["elem"], oneshot=True,
+                               stream=pair.stream)
+            pair.plan.fill(h, pair.tv, pair.seed, kind=pair.w["elem"], stream=pair.stream)
+            pair.plan.wait(10.0)
+        finally:
+            pair.close()
+    # Byte-range chunks over a view read with a row stride the plan was not
+    # cut for: the fill's contiguity check refuses it before any launch.
+    w = dict(workloads.SMALL["u32_chunks_ragged_p3"])
+    pair = Pair(w)
+    try:
+        h = pair.plan.start(pair.stream)
+        strided = [tc.View(v.byte_offset, v.rows // 2, v.cols // 2, v.cols, v.elem_bytes, 0)
+                   for v in pair.tv]
+        with pytest.raises(tc.InvalidArgument, match="contiguous views"):
+            pair.plan.fill(h, strided, pair.seed, kind=w["elem"], oneshot=True, stream=pair.stream)
+        pair.plan.fill(h, pair.tv, pair.seed, kind=w["elem"], oneshot=True, stream=pair.stream)
+        pair.plan.wait(10.0)
+        pair.oracle_round()
+        pair.compare("oneshot after a refused call")
+    finally:
+        pair.close()
+
+
 def _expected_replicas(pair, r):
     """Every replica after round r delivered in full (oracle)."""
     pair.oracle_round()

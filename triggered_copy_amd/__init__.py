@@ -16,7 +16,7 @@ import numpy as np
 
 from . import _lib
 from ._lib import (FILL_BF16, FILL_U8, FILL_U32, MARK_INKERNEL, MARK_NONE,  # noqa: F401
-                   FILL_PARALLEL, FILL_SERIAL, FILL_WAVES,
+                   FILL_PARALLEL, FILL_SERIAL, FILL_WAVES, FILL_ONESHOT,
                    GATE_ROW_BYTES, TC_MAX_RANKS, Handle, View)
 
 __all__ = ["View", "Schedule", "whole", "chunks", "tile_chunks", "from_arrays", "order_grouped",
@@ -393,10 +393,12 @@ class TriggeredPlan:
 
     # -- synthetic producers / consumer on this plan
     def fill(self, handle, views, seed, kind="u32", mark=True, serial=False, order=None,
-             order_stride=0, waves=False, ctas=0, stream=None):
+             order_stride=0, waves=False, ctas=0, oneshot=False, stream=None):
         """Hash-fill producer.  serial: one CTA per rank in order[];
         waves: a persistent grid of `ctas` CTAs completing every rank's
-        chunk 0, then every rank's chunk 1, ...; otherwise one CTA per
+        chunk 0, then every rank's chunk 1, ...; oneshot: one CTA per
+        16 KiB block of every writer's share, in the waves order (plans of
+        byte-range chunks and contiguous views only); otherwise one CTA per
         writer."""
         kinds = {"u32": FILL_U32, "bf16": FILL_BF16, "u8": FILL_U8}
         va = (View * self.P)(*[_as_view(v, None) for v in views])
@@ -405,7 +407,10 @@ class TriggeredPlan:
         d.seed = seed
         d.kind = kinds[kind]
         d.mark_mode = MARK_INKERNEL if mark else MARK_NONE
-        d.mode = FILL_SERIAL if serial else FILL_WAVES if waves else FILL_PARALLEL
+        if serial + waves + oneshot > 1:
+            raise ValueError("fill: pick one of serial, waves, oneshot")
+        d.mode = (FILL_SERIAL if serial else FILL_WAVES if waves else
+                  FILL_ONESHOT if oneshot else FILL_PARALLEL)
         d.order = order.data_ptr() if order is not None else None
         d.order_stride = order_stride
         d.ctas = ctas

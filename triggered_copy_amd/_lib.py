@@ -14,7 +14,7 @@ OK, EINVAL, EBOUNDS, EOVERLAP, ENOMEM, EHIP, ESTATE, ETIMEOUT, EEXTRA, EROUNDS, 
 STATE_NAMES = {0: "READY", 1: "STARTED", 2: "DONE", 3: "FAILED", 4: "CLOSED", 5: "CLOSING"}
 CHECK_OWN_ROWS = 1
 FILL_U32, FILL_BF16, FILL_U8 = 0, 1, 2
-FILL_PARALLEL, FILL_SERIAL, FILL_WAVES = 0, 1, 2
+FILL_PARALLEL, FILL_SERIAL, FILL_WAVES, FILL_ONESHOT = 0, 1, 2, 3
 MARK_INKERNEL, MARK_NONE = 0, 1
 
 u32, u64, vp = C.c_uint32, C.c_uint64, C.c_void_p

@@ -54,6 +54,18 @@ static_assert(sizeof(ChunkD) == 32, "chunk descriptor is 32 bytes");
 // ends: the chunk is one contiguous byte range.
 constexpr uint32_t kChunkContiguous = 1;
 
+// One-shot fill: a writer's share of a contiguous chunk is written by
+// ceil(bytes / kOneShotBlock) one-block CTAs.  Shares are listed every
+// rank's chunk 0 first, then chunk 1, ...; `first_block` is the prefix sum of
+// the blocks of the shares before (the entry past the last holds the total).
+constexpr uint64_t kOneShotBlock = 16384;
+struct ShareD {
+  uint64_t first_block;
+  uint64_t off, bytes;   // the share's byte range in its rank's replica
+  uint32_t g, j;         // global chunk, writer index
+};
+static_assert(sizeof(ShareD) == 32, "ShareD layout");
+
 // Cuts every rank's regions into pieces of about piece_bytes (whole rows for
 // 2-D regions; a linear region into piece_bytes ranges).
 void build_pieces(uint32_t nranks, const tc_schedule* const* sched, uint64_t piece_bytes,

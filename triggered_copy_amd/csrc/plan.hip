@@ -62,7 +62,7 @@ namespace tc {
 
 // ------------------------------------------------------------ layout
 
-Layout compute_layout(uint32_t P, uint32_t G, uint64_t npieces) {
+Layout compute_layout(uint32_t P, uint32_t G, uint64_t npieces, uint64_t nwriters) {
   Layout L{};
   uint64_t off = 0;
   auto take = [&](uint64_t bytes) {
@@ -86,6 +86,8 @@ Layout compute_layout(uint32_t P, uint32_t G, uint64_t npieces) {
   L.round_blk[0] = take(L.round_bytes);
   L.round_blk[1] = take(L.round_bytes);
   L.status = take(256);
+  L.shares = take((nwriters + 1) * sizeof(ShareD));
+  L.share_ctr = take(nwriters * 64);  // one counter per 64-byte line
   L.total = off;
   return L;
 }
@@ -642,7 +644,9 @@ int tc_plan_workspace_bytes(uint32_t nranks, const tc_schedule* const* schedules
   std::vector<ChunkD> chunks;
   std::vector<uint32_t> pb, cb;
   build_pieces(nranks, schedules, piece_bytes, pieces, chunks, pb, cb);
-  *out_bytes = compute_layout(nranks, (uint32_t)chunks.size(), pieces.size()).total;
+  uint64_t nw = 0;
+  for (const ChunkD& c : chunks) nw += c.writers;
+  *out_bytes = compute_layout(nranks, (uint32_t)chunks.size(), pieces.size(), nw).total;
   return TC_OK;
 }
 
@@ -732,7 +736,8 @@ int tc_plan_create(const tc_plan_desc* d, tc_plan** out) {
   const uint64_t piece_bytes = d->piece_bytes ? d->piece_bytes : kDefaultPieceBytes;
   build_pieces(P->P, d->schedules, piece_bytes, P->pieces, P->chunks, P->piece_base, P->chunk_base);
   P->G = (uint32_t)P->chunks.size();
-  P->L = compute_layout(P->P, P->G, P->pieces.size());
+  for (const ChunkD& c : P->chunks) P->total_writers += c.writers;
+  P->L = compute_layout(P->P, P->G, P->pieces.size(), P->total_writers);
   if (P->L.total > d->workspace_bytes) {
     const uint64_t need = P->L.total;
     delete P;
@@ -807,6 +812,47 @@ int tc_plan_create(const tc_plan_desc* d, tc_plan** out) {
     TC_HIP_C(hipMemcpy(P->ws + P->L.writers, writers.data(), P->G * 4, hipMemcpyHostToDevice));
   }
   TC_HIP_C(hipMemcpy(P->ws + P->L.wprefix, wprefix.data(), wprefix.size() * 8, hipMemcpyHostToDevice));
+
+  // One-shot fill table, when every chunk is one byte range: each writer's
+  // share cut into kOneShotBlock blocks, every rank's chunk 0 first, then
+  // chunk 1, ... (an empty share still gets one block, which issues its
+  // writer's mark).
+  bool all_ranges = P->G > 0;
+  for (const ChunkD& c : P->chunks)
+    if (!(c.flags & kChunkContiguous)) all_ranges = false;
+  if (all_ranges) {
+    std::vector<ShareD> sh;
+    uint32_t maxc = 0;
+    for (uint32_t p = 0; p < P->P; ++p) maxc = std::max(maxc, P->chunk_base[p + 1] - P->chunk_base[p]);
+    uint64_t blocks = 0;
+    for (uint32_t c = 0; c < maxc; ++c)
+      for (uint32_t p = 0; p < P->P; ++p) {
+        if (c >= P->chunk_base[p + 1] - P->chunk_base[p]) continue;
+        const uint32_t g = P->chunk_base[p] + c;
+        const ChunkD& cd = P->chunks[g];
+        for (uint32_t j = 0; j < cd.writers; ++j) {
+          const uint64_t lo = (uint64_t)j * cd.npieces / cd.writers;
+          const uint64_t hi = (uint64_t)(j + 1) * cd.npieces / cd.writers;
+          ShareD d{};
+          d.first_block = blocks;
+          d.g = g;
+          d.j = j;
+          if (lo < hi) {
+            const PieceD& a = P->pieces[cd.first_piece + lo];
+            const PieceD& b = P->pieces[cd.first_piece + hi - 1];
+            d.off = a.off;
+            d.bytes = b.off + b.row_bytes - a.off;
+          }
+          blocks += d.bytes ? (d.bytes + kOneShotBlock - 1) / kOneShotBlock : 1;
+          sh.push_back(d);
+        }
+      }
+    ShareD end{};
+    end.first_block = blocks;
+    sh.push_back(end);
+    TC_HIP_C(hipMemcpy(P->ws + P->L.shares, sh.data(), sh.size() * sizeof(ShareD), hipMemcpyHostToDevice));
+    P->oneshot_blocks = blocks;
+  }
 
   // Default engine size: one worker wave per piece up to 256 (small rounds
   // are latency-bound: every piece in flight at once), otherwise one wave per

@@ -32,10 +32,11 @@ struct Layout {
   uint64_t launch[2], launch_bytes;     // tickets | stats | stop | done, per launch parity
   uint64_t round_blk[2], round_bytes;   // sig | cursors, per round parity
   uint64_t status;
+  uint64_t shares, share_ctr;           // one-shot fill: share table and per-share counters
   uint64_t total;
 };
 
-Layout compute_layout(uint32_t P, uint32_t G, uint64_t npieces);
+Layout compute_layout(uint32_t P, uint32_t G, uint64_t npieces, uint64_t nwriters);
 
 }  // namespace tc
 
@@ -51,6 +52,7 @@ struct tc_plan {
   std::vector<uint32_t> piece_base, chunk_base;
   uint64_t total_writers = 0;
   uint64_t bytes_read = 0, bytes_moved = 0;
+  uint64_t oneshot_blocks = 0;  // one-shot fill grid (0: some chunk is not one byte range)
 
   int device = 0;
   hipStream_t engine_stream = nullptr;

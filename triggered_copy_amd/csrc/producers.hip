@@ -48,6 +48,9 @@ struct FillArgs {
   uint32_t contiguous;                 // bit p: view p has row_stride == cols
   uint32_t kind, mark, elem;
   uint32_t order_stride, G, max_chunks, pad1;
+  const tc::ShareD* shares;            // one-shot mode: nshares + 1 entries
+  uint64_t* share_ctr;                 // one-shot mode: blocks done per share (8 per 64 B)
+  uint64_t nshares;
 };
 
 // mix64(k ^ mix64(seed)) for k = (p << 48) | (round << 32) | idx, idx < 2^32.
@@ -92,11 +95,26 @@ __device__ inline uint64_t index_at(const FillArgs& a, uint32_t p, uint64_t off)
   return r * a.view_cols[p] + (rel - r * a.view_pitch[p]) / a.elem;
 }
 
+// Byte `at` of a range starting at d: a plain store, or a write-through
+// buffer store through `wt` (the same range's descriptor).
+template <bool kWriteThrough>
+__device__ inline void put_byte(uint8_t* d, __amdgpu_buffer_rsrc_t wt, uint32_t at, uint8_t v) {
+  if (kWriteThrough)
+    __builtin_amdgcn_raw_buffer_store_b8(v, wt, (int)at, 0, 17 /* sc0 sc1 */);
+  else
+    d[at] = v;
+}
+
 // Whole CTA: write the values of `len` bytes at `off` (within one view row,
-// or anywhere in a contiguous view) of replica p.
-__device__ void fill_range(const FillArgs& a, uint32_t p, uint64_t off, uint64_t len) {
+// or anywhere in a contiguous view) of replica p; idx0 is the view element
+// index of byte `off`.  With kWriteThrough the stores go through to memory
+// at system scope (len < 2^31), so that once they complete the bytes are
+// visible to every CU without an L2 write-back.
+template <bool kWriteThrough>
+__device__ void fill_span(const FillArgs& a, uint32_t p, uint64_t off, uint64_t len, uint64_t idx0) {
   uint8_t* base = reinterpret_cast<uint8_t*>(a.rep[p]);
-  const uint64_t idx0 = index_at(a, p, off);
+  const __amdgpu_buffer_rsrc_t wt =
+      __builtin_amdgcn_make_buffer_rsrc(base + off, 0, kWriteThrough ? (int)len : 0, 0x00020000);
   const KeyHash kh = key_hash_setup(a, p);
   const uint32_t e = a.elem;
   if (((off | len) & 15) == 0) {
@@ -123,25 +141,34 @@ __device__ void fill_range(const FillArgs& a, uint32_t p, uint64_t off, uint64_t
           out[k] = w;
         }
       }
-      dst[v] = out;
+      if (kWriteThrough)
+        __builtin_amdgcn_raw_buffer_store_b128(out, wt, (int)(v * 16), 0, 17 /* sc0 sc1 */);
+      else
+        dst[v] = out;
     }
   } else {
     const uint64_t n = len / e;
+    uint8_t* d = base + off;
     for (uint64_t i = threadIdx.x; i < n; i += kFillThreads) {
       const uint64_t h = key_hash(kh, (uint32_t)(idx0 + i));
-      uint8_t* d = base + off + i * e;
+      const uint32_t at = (uint32_t)(i * e);
       if (a.kind == TC_FILL_U32) {
         const uint32_t v = (uint32_t)h;
-        for (uint32_t b = 0; b < 4; ++b) d[b] = (uint8_t)(v >> (8 * b));
+#pragma unroll
+        for (uint32_t b = 0; b < 4; ++b) put_byte<kWriteThrough>(d, wt, at + b, (uint8_t)(v >> (8 * b)));
       } else if (a.kind == TC_FILL_BF16) {
         const uint32_t v = bf16_of(h);
-        d[0] = (uint8_t)v;
-        d[1] = (uint8_t)(v >> 8);
+        put_byte<kWriteThrough>(d, wt, at, (uint8_t)v);
+        put_byte<kWriteThrough>(d, wt, at + 1, (uint8_t)(v >> 8));
       } else {
-        d[0] = (uint8_t)h;
+        put_byte<kWriteThrough>(d, wt, at, (uint8_t)h);
       }
     }
   }
+}
+
+__device__ void fill_range(const FillArgs& a, uint32_t p, uint64_t off, uint64_t len) {
+  fill_span<false>(a, p, off, len, index_at(a, p, off));
 }
 
 __device__ void fill_piece(const FillArgs& a, uint32_t p, const tc::PieceD& pc) {
@@ -221,6 +248,45 @@ __global__ __launch_bounds__(kFillThreads) void fill_waves_kernel(FillArgs a) {
       }
       slot += w;
     }
+  }
+}
+
+// One-shot grid: CTA b writes block b of the share table (kOneShotBlock
+// bytes of one writer's share of a contiguous chunk) with write-through
+// stores.  The share's blocks count themselves on a wrapping counter; the
+// block that completes the count issues the writer's mark, so each writer
+// slot still marks its chunk exactly once per round.  Counting happens only
+// when the fill marks: a deferred-mark fill leaves the counters at zero.
+__global__ __launch_bounds__(kFillThreads) void fill_oneshot_kernel(FillArgs a) {
+  const uint64_t b = blockIdx.x;
+  uint64_t lo = 0, hi = a.nshares;  // largest s with shares[s].first_block <= b
+  while (hi - lo > 1) {
+    const uint64_t mid = (lo + hi) / 2;
+    if (a.shares[mid].first_block <= b) lo = mid; else hi = mid;
+  }
+  const tc::ShareD sh = a.shares[lo];
+  const uint64_t nb = a.shares[lo + 1].first_block - sh.first_block;
+  const uint64_t at = (b - sh.first_block) * tc::kOneShotBlock;
+  if (at < sh.bytes) {
+    // Contiguous view: the element index is the byte distance over the element size.
+    const uint32_t p = a.chunks[sh.g].rank;
+    const uint64_t rel = sh.off + at - a.view_off[p];
+    const uint64_t idx0 = a.elem == 4 ? rel >> 2 : a.elem == 2 ? rel >> 1 : rel;
+    fill_span<true>(a, p, sh.off + at, min(tc::kOneShotBlock, sh.bytes - at), idx0);
+  }
+  if (a.mark != TC_MARK_INKERNEL) return;
+  __shared__ uint32_t last;
+  __builtin_amdgcn_s_waitcnt(TC_WAITCNT_VMCNT0);  // this wave's write-through stores are in memory
+  __syncthreads();                                // ... and every other wave's
+  if (tc_is_cta_leader()) {
+    uint32_t* ctr = reinterpret_cast<uint32_t*>(a.share_ctr + lo * 8);
+    const uint32_t old = __builtin_amdgcn_atomic_inc32(ctr, (uint32_t)nb - 1, __ATOMIC_RELAXED, "agent");
+    last = old == (uint32_t)nb - 1;
+  }
+  __syncthreads();
+  if (tc_uniform(last)) {
+    const tc::ChunkD cd = a.chunks[sh.g];
+    tc_mark_ready_wt(a.h, cd.rank, cd.local);
   }
 }
 
@@ -341,6 +407,17 @@ int tc_produce_fill(tc_plan* P, const tc_handle* h, const tc_fill_desc* d, void*
     for (uint32_t p = 0; p < P->P; ++p)
       a.max_chunks = std::max(a.max_chunks, P->chunk_base[p + 1] - P->chunk_base[p]);
     hipLaunchKernelGGL(fill_waves_kernel, dim3(ctas), dim3(kFillThreads), 0, s, a);
+  } else if (d->mode == TC_FILL_ONESHOT) {
+    if (P->total_writers == 0) return TC_OK;
+    if (P->oneshot_blocks == 0) return fail(TC_EINVAL, "fill: one-shot mode needs every chunk to be one byte range");
+    for (uint32_t p = 0; p < P->P; ++p)
+      if (P->chunk_base[p + 1] > P->chunk_base[p] && !(a.contiguous & (1u << p)))
+        return fail(TC_EINVAL, "fill: one-shot mode needs contiguous views");
+    if (P->oneshot_blocks > 0x7FFFFFFFull) return fail(TC_EINVAL, "fill: too many one-shot blocks");
+    a.shares = reinterpret_cast<const tc::ShareD*>(P->ws + P->L.shares);
+    a.share_ctr = reinterpret_cast<uint64_t*>(P->ws + P->L.share_ctr);
+    a.nshares = P->total_writers;
+    hipLaunchKernelGGL(fill_oneshot_kernel, dim3((uint32_t)P->oneshot_blocks), dim3(kFillThreads), 0, s, a);
   } else {
     return fail(TC_EINVAL, "fill: unknown mode");
   }
