@@ -421,10 +421,12 @@ def run_barrier(torch, tc, workloads):
     return dict(us_per_generation=statistics.median(res), P=P, generations=G)
 
 
-def run_small_round(torch, tc, workloads, seed, name, rounds, premark=False):
+def run_small_round(torch, tc, workloads, seed, name, rounds, premark=False, oneshot=False):
     """Full rounds of a small workload: start, the fill with in-kernel marks,
     wait.  With premark (for counter collection, which runs kernels one at
-    a time) the fill and its marks precede start()."""
+    a time) the fill and its marks precede start().  The fill is one CTA per
+    writer (the workload's producer as specified), or with oneshot one CTA
+    per 16 KiB block, each writer's share still marked once."""
     w = workloads.FULL[name]
     views, rep, B = rank_setup(w, torch, tc)
     plan = tc.TriggeredPlan(rep, build_sched(w, views, tc))
@@ -434,12 +436,12 @@ def run_small_round(torch, tc, workloads, seed, name, rounds, premark=False):
         a = time.perf_counter()
         if premark:
             h = plan.current_handle()
-            plan.fill(h, views, seed, kind=w["elem"], mark=False, stream=prod)
+            plan.fill(h, views, seed, kind=w["elem"], mark=False, oneshot=oneshot, stream=prod)
             plan.mark_all(h, stream=prod)
             plan.start(prod)
         else:
             h = plan.start(prod)
-            plan.fill(h, views, seed, kind=w["elem"], mark=True, stream=prod)
+            plan.fill(h, views, seed, kind=w["elem"], mark=True, oneshot=oneshot, stream=prod)
         plan.wait(30.0)
         plan.next_round()
         if i >= 5:
@@ -594,6 +596,10 @@ def main():
         log("small rounds")
         extras["bf16_chunks_p2_round"] = run_small_round(torch, tc, workloads, BASE_SEED, "bf16_chunks_p2", 200)
         extras["u32_whole_p8_round"] = run_small_round(torch, tc, workloads, BASE_SEED, "u32_whole_p8", 50)
+        extras["bf16_chunks_p2_round_oneshot_fill"] = run_small_round(
+            torch, tc, workloads, BASE_SEED, "bf16_chunks_p2", 200, oneshot=True)
+        extras["u32_whole_p8_round_oneshot_fill"] = run_small_round(
+            torch, tc, workloads, BASE_SEED, "u32_whole_p8", 50, oneshot=True)
         extras["overlapped_triggered_round"] = {"ms": h.get("overlapped_round_ms"),
                                                 "delivered_gbs": h.get("overlapped_delivered_gbs")}
         if args.workload == "u32_chunks_1p5g_p4":
