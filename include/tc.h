@@ -355,8 +355,9 @@ enum { TC_MARK_INKERNEL = 0, TC_MARK_NONE = 1 };
  *   ONESHOT:  one CTA per 16 KiB block of every writer's share, blocks in
  *             the WAVES order, stores written through to memory; the last
  *             block of a share to finish issues that writer's mark.  Only
- *             for plans whose every chunk is one byte range and for
- *             contiguous views (else TC_EINVAL). */
+ *             for plans whose every chunk is one byte range, with fewer
+ *             than 2^31 blocks, and for contiguous views (else TC_EINVAL).
+ *             A deferred-mark (TC_MARK_NONE) one-shot fill counts nothing. */
 enum { TC_FILL_PARALLEL = 0, TC_FILL_SERIAL = 1, TC_FILL_WAVES = 2, TC_FILL_ONESHOT = 3 };
 
 typedef struct tc_fill_desc {
