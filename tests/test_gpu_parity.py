@@ -258,11 +258,16 @@ def _swap_in(pair, tsched, osched_list, **plan_kw):
     pair.sim = oplan.PlanSim(pair.sim.rep, osched_list)
 
 
-def _rounds(pair, n, what):
+def _rounds(pair, n, what, deferred=(), **fill_kw):
+    """n rounds of fill, wait and oracle comparison; rounds listed in
+    ``deferred`` fill without marks, then issue them with the mark kernel."""
     for r in range(1, n + 1):
         log(f"{what} round {r}")
         h = pair.plan.start(pair.stream)
-        pair.plan.fill(h, pair.tv, pair.seed, kind=pair.w["elem"], stream=pair.stream)
+        pair.plan.fill(h, pair.tv, pair.seed, kind=pair.w["elem"], mark=r not in deferred,
+                       stream=pair.stream, **fill_kw)
+        if r in deferred:
+            pair.plan.mark_all(h, stream=pair.stream)
         pair.plan.wait(10.0)
 
         def produce(p, rr):
@@ -370,6 +375,43 @@ def test_random_hand_built_tables(case):
         log(f"random tables case {case}: P={P} rows={rows} cols={cols} {kw}")
         _swap_in(pair, ts, os_, **kw)
         _rounds(pair, 2, f"random tables case {case}")
+    finally:
+        pair.close()
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_byte_range_tables_oneshot_fill(case):
+    # Every rank's bytes cut at random points into linear regions, grouped
+    # into chunks of 1-3 adjacent regions with 1-6 writers (more writers
+    # than pieces leaves empty shares), random piece sizes: the one-shot
+    # fill's share and block tables against the oracle over 3 rounds, the
+    # second with deferred marks.
+    from oracle import schedule as osched
+    rng = np.random.default_rng(3000 + case)
+    P = int(rng.integers(2, 6))
+    cols = int(rng.integers(700, 5000))
+    rows = int(rng.integers(1, 60))
+    w = dict(P=P, rows=rows, cols=cols, elem="u8", builder="whole", writers=1, rounds=3)
+    pair = Pair(w, seed=BASE_SEED + 11 * case)
+    try:
+        ts, os_ = [], []
+        n = rows * cols
+        for p in range(P):
+            cuts = sorted(set(rng.integers(1, n, size=int(rng.integers(0, 9))).tolist()))
+            edges = [0] + cuts + [n]
+            regions = [(p * n + a, 1, b - a, 0) for a, b in zip(edges[:-1], edges[1:])]
+            chunks, at = [], 0
+            while at < len(regions):
+                k = min(int(rng.integers(1, 4)), len(regions) - at)
+                chunks.append((at, k, int(rng.integers(1, 7))))
+                at += k
+            ts.append(tc.from_arrays(chunks, regions))
+            os_.append(osched.from_tables(chunks, regions))
+        kw = dict(piece_bytes=int(rng.choice([256, 4096, 8192, 65536])),
+                  engine_ctas=int(rng.integers(1, 9)))
+        log(f"random byte-range tables case {case}: P={P} bytes/rank={n} {kw}")
+        _swap_in(pair, ts, os_, **kw)
+        _rounds(pair, 3, f"random byte ranges case {case}", deferred=(2,), oneshot=True)
     finally:
         pair.close()
 
