@@ -26,7 +26,7 @@
 
 #define P 3
 #define ROWS 40
-#define COLS 96
+#define COLS 960
 #define SENTINEL 0xA5
 
 #define CHECK_TC(call)                                                              \
@@ -92,7 +92,7 @@ int main(void) {
   CHECK_HIP(hipStreamCreateWithFlags(&stream, hipStreamNonBlocking));
 
   tc_gate_row gates[P * P];  /* P tables x G = P chunks */
-  for (uint32_t round = 1; round <= 2; ++round) {
+  for (uint32_t round = 1; round <= 3; ++round) {
     tc_handle h;
     CHECK_TC(tc_plan_start(plan, stream, &h));
     tc_fill_desc f;
@@ -101,7 +101,7 @@ int main(void) {
     f.seed = 0x7C0FFEEull;
     f.kind = TC_FILL_U32;
     f.mark_mode = TC_MARK_INKERNEL;
-    f.mode = TC_FILL_PARALLEL;
+    f.mode = round == 1 ? TC_FILL_PARALLEL : TC_FILL_ONESHOT;  /* one CTA per writer, then per 16 KiB */
     CHECK_TC(tc_produce_fill(plan, &h, &f, stream));
     CHECK_TC(tc_plan_wait(plan, 10u * 1000u * 1000u));
     CHECK_HIP(hipDeviceSynchronize());
@@ -155,6 +155,6 @@ int main(void) {
   CHECK_HIP(hipFree(ws));
   CHECK_HIP(hipStreamDestroy(stream));
   free(prev);
-  printf("c_abi round_trip: OK (3 ranks, 2 rounds)\n");
+  printf("c_abi round_trip: OK (3 ranks, 3 rounds)\n");
   return 0;
 }

@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 def test_plain_c_round_trip(tmp_path):
     require_gpu()
     exe = c_abi_build.build(str(tmp_path))
-    log("c_abi round_trip: 3 ranks, 2 rounds")
+    log("c_abi round_trip: 3 ranks, 3 rounds")
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "OK" in r.stdout
