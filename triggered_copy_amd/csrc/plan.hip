@@ -913,10 +913,25 @@ int tc_plan_wait(tc_plan* P, uint64_t timeout_us) {
     if (int rc = launch_engine(P)) return rc;
     P->need_relaunch = false;
   }
-  // One event covers everything: the check runs after the engine and after
-  // the producer's work, so extra marks issued after the gate opened count.
-  if (int rc = queue_check(P)) return rc;
   const auto deadline = std::chrono::steady_clock::now() + std::chrono::microseconds(timeout_us);
+  // The check must follow the producer's work too, so that extra marks issued
+  // after a gate opened count.  Waiting here, on the host, for the producer's
+  // stream to drain lets the check follow the engine alone on its stream; a
+  // device-side dependency on the other stream starts it about 4 us later.
+  // Past the deadline the dependency is put on the device after all.  The
+  // queries are spaced 2 us apart: back to back, they slowed the kernels
+  // running meanwhile (GEMM producers beside the engine) by about 2%.
+  for (;;) {
+    const hipError_t q = hipStreamQuery(P->producer_stream);
+    if (q == hipSuccess) break;
+    if (q != hipErrorNotReady) return hip_fail(q, "hipStreamQuery(producer stream)");
+    const auto now = std::chrono::steady_clock::now();
+    if (now >= deadline) break;
+    const auto next = now + std::chrono::microseconds(2);
+    while (std::chrono::steady_clock::now() < next) {
+    }
+  }
+  if (int rc = queue_check(P)) return rc;
   const uint32_t seq = P->check_seq;
   const bool timed_out = check_done_by(P, seq, deadline) == 0;
   if (timed_out) {
