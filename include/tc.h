@@ -112,12 +112,15 @@ typedef struct tc_chunk {
  * marks); in a peer q's table the same row holds arrival (= rounds delivered
  * to q).  Bytes 24..63 are zero.
  *
- * On the device only `arrival` is stored in the rows.  The writer count is
+ * On the device the rows hold `ready` and `arrival`.  The writer count is
  * kept in TC_MARK_STRIPES counters per chunk, TC_MARK_STRIPE_BYTES apart, so
  * that the marks of many CTAs finishing together do not queue on one
- * address; a mark adds 1 to one of them.  The count is their sum, the gate
- * of round r is open when the count reaches r * writers, and `ready` is the
- * derived value min(count / writers, round). */
+ * address; a mark adds 1 to one of them.  The count is their sum and the
+ * gate of round r is open when it reaches r * writers.  Nobody learns that
+ * its mark was the last: the copy engine, which sums the stripes, stores r
+ * into `ready` when it finds the gate open, before it signals the chunk.
+ * tc_plan_read_gates reports the device words, with the writer counter as
+ * the stripes' sum. */
 typedef struct tc_gate_row {
   uint64_t ready;
   uint64_t arrival;
@@ -209,10 +212,11 @@ typedef struct tc_plan_desc {
   uint64_t rows_per_rank_bytes;        /* for TC_CHECK_OWN_ROWS */
   const uint32_t* cu_mask;             /* NULL = copy engine may use every CU */
   uint32_t cu_mask_words;
-  uint32_t engine_ctas;                /* CTAs of 4 worker waves; 0 = one wave per 192 KiB of
+  uint32_t engine_ctas;                /* CTAs of 4 waves (wave 0 of the grid publishes the
+                                          gates, the others copy); 0 = one wave per 192 KiB of
                                           delivered bytes per round (source bytes times the
-                                          P - 1 receivers), at least one per piece up to 256,
-                                          at most 16 waves per usable CU */
+                                          P - 1 receivers), at least one per piece up to 256
+                                          plus the publisher, at most 16 waves per usable CU */
   uint64_t piece_bytes;                /* copy work unit, multiple of 256, <= 1 GiB; 0 = 8 KiB */
   uint64_t engine_backstop_us;         /* engine gives up after this long; 0 = 30 s */
 } tc_plan_desc;
@@ -281,35 +285,62 @@ int tc_plan_wait(tc_plan* plan, uint64_t timeout_us);
 int tc_plan_next_round(tc_plan* plan);
 
 /* Closes the plan ([TP] Model: close / leaving the with block; The kernel
- * author's contract: closing mid-round).  Safe in any state.  In the middle
- * of a round every gate of the plan is forced open, so the copy engine
- * delivers every chunk with whatever bytes it holds at that moment (after a timeout it is run again for
- * that); then its streams, events and host words are freed.  The caller's
- * buffers keep what was delivered.  Plans with the same CU mask share one
- * engine stream, so their rounds run in start() order; a plan whose engine
- * is still queued behind another plan's waiting engine cannot finish first.
- * With closing != NULL such a close() returns TC_OK with *closing = 1 and the
- * plan CLOSING (still valid): closing the earlier plan lets it finish, and a
+ * author's contract: prepared copies cannot be withdrawn, so closing a plan
+ * in the middle of a round, or before it starts, sends each rank's chunks as
+ * they stand).  Safe in any state.  STARTED (or CLOSING) and READY: every
+ * gate of the plan is forced open and the copy engine delivers every chunk
+ * with whatever bytes it holds when its copy runs (the engine is launched
+ * for a READY round, and run again after a timeout); DONE and FAILED: there
+ * is nothing left to send.  Then its streams, events and host words are
+ * freed; the caller's buffers keep what was delivered.
+ * Plans with the same CU mask share one engine stream, so their rounds run
+ * in start() order, and a plan whose engine is queued behind another plan's
+ * waiting engine cannot finish first.  With closing != NULL, close() waits
+ * for the engine as long as every earlier plan's unfinished engine on the
+ * stream can finish by itself (all its gates open, or forced); once one
+ * waits on shut gates, close() returns TC_OK with *closing = 1 and the plan
+ * CLOSING (still valid): closing the earlier plan lets it finish, and a
  * later tc_plan_close frees it.  Otherwise (*closing = 0) the plan is freed.
- * With closing == NULL the call waits for the engine.  TC_ETIMEOUT when the
- * engine does not stop within 10 s (the plan is then leaked, not freed). */
+ * With closing == NULL the call just waits for the engine.  TC_ETIMEOUT when
+ * the engine does not stop within 10 s (the plan is then leaked, not
+ * freed). */
 int tc_plan_close(tc_plan* plan, int* closing);
 
+/* The plan's state and current round ([TP] Model: a round is start(), the
+ * producer's marks, wait(); Gates and rounds: rounds start at 1 and grow by
+ * one per next_round(); The kernel author's contract: a plan with extra
+ * marks is FAILED and only closes, and a close() queued behind an earlier
+ * plan's waiting copies leaves the plan CLOSING).  Either output may be
+ * NULL.  TC_EINVAL for a NULL plan. */
 int tc_plan_state(const tc_plan* plan, int* state, uint32_t* round);
 
-/* After TC_ETIMEOUT / TC_EEXTRA: up to cap (rank, chunk) pairs, as
- * rank_chunk[2i], rank_chunk[2i+1]; *n = the total number. */
+/* The chunks the last wait() found wrong ([TP] The kernel author's
+ * contract, item 2: wait() raises when a chunk got extra marks, and a
+ * timeout names the chunks still short).  After TC_EEXTRA: the chunks with
+ * extra marks; after TC_ETIMEOUT: the chunks not marked by all their writers
+ * or not yet arrived at every peer; after TC_ECORRUPT: the chunks whose rows
+ * hold impossible counts; empty after TC_OK.  Up to cap (rank, chunk) pairs,
+ * as rank_chunk[2i], rank_chunk[2i+1] (host, may be NULL with cap 0);
+ * *n = the total number. */
 int tc_plan_problems(const tc_plan* plan, uint32_t* rank_chunk, uint32_t cap, uint32_t* n);
 
-/* Synchronous snapshot of all gate tables: P x G x 64 bytes into host, rows
- * as tc_gate_row describes (ready and writers derived from the mark stripes
- * against the plan's current round). */
+/* Synchronous snapshot of all gate tables ([TP] Gates and rounds): P x G x
+ * 64 bytes into host, rows as tc_gate_row describes (ready and arrival as
+ * stored on the device, writers = the sum of the chunk's mark stripes).
+ * TC_EINVAL when bytes < P * G * 64. */
 int tc_plan_read_gates(tc_plan* plan, void* host, uint64_t bytes);
 
-/* Synchronous snapshot of the queue cursors: host[p*P + q] = chunks of rank
- * p delivered to rank q so far this round (0 on the diagonal). */
+/* Synchronous snapshot of the queue cursors ([TP] The kernel author's
+ * contract, item 1: a rank's copies to one peer share one queue and complete
+ * strictly in schedule order, so how far a queue has got is one number):
+ * host[p*P + q] = chunks of rank p delivered to rank q so far this round
+ * (0 on the diagonal), P x P uint32 in host memory. */
 int tc_plan_read_cursors(tc_plan* plan, uint32_t* host);
 
+/* Per-round figures of the copy side, for benchmarks ([TP] opening
+ * paragraph: the copy side moves each chunk to every peer and signals its
+ * arrival there; Model: a round is one use of the plan).  Reads the last
+ * engine launch's events and counters (synchronously, after wait()). */
 typedef struct tc_stats {
   float engine_ms;         /* last copy-engine launch, HIP events on its stream */
   uint32_t launches;       /* copy-engine launches this round (1 + resumes) */
@@ -324,10 +355,13 @@ typedef struct tc_stats {
 
 int tc_plan_stats(tc_plan* plan, tc_stats* out);
 
-/* The copy engine's stream (hipStream_t), for timing. */
+/* The copy engine's stream (hipStream_t), for timing kernels on it with
+ * events: the engine is the plan's copy side ([TP] opening paragraph). */
 int tc_plan_engine_stream(tc_plan* plan, void** stream);
 
-/* Test hook: set the round of a DONE plan (exercises the round limit). */
+/* Test hook: set the round of a DONE plan, to exercise the round limit
+ * without 2^32 rounds ([TP] Gates and rounds: gates are never reset, so a
+ * plan runs at most 2^32 - 1 rounds).  TC_ESTATE unless DONE or round 0. */
 int tc_plan_debug_set_round(tc_plan* plan, uint32_t round);
 
 /* ------------------------------------------------ synthetic producers */
@@ -477,6 +511,16 @@ int tc_barrier_run(int32_t* W, uint32_t P, uint32_t first_gen, uint32_t n_gen,
                    uint32_t* status, void* stream);
 
 /* ------------------------------------------------------------- misc */
+
+/* Releases what the library keeps for the life of the process: the copy
+ * engines' CU-masked streams (one per device and CU mask, shared by plans;
+ * the plan's engine of [TP] Model and opening paragraph).  Call it after the
+ * last plan is closed and before the HIP runtime shuts down (the Python
+ * binding does so at interpreter exit), so that no stream outlives the
+ * runtime's own teardown.  Later plans create streams again.  TC_ESTATE while
+ * any plan is open (nothing is released then); TC_EHIP when a stream cannot
+ * be destroyed. */
+int tc_release(void);
 
 const char* tc_last_error(void);
 const char* tc_version(void);

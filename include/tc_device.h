@@ -179,6 +179,57 @@ __device__ inline bool tc_wait(const tc_handle& h, uint32_t dst, uint32_t src, u
   return ok;
 }
 
+/* ---------------------------------------------------------------- barrier
+ *
+ * Dedicated-row signals ([BAR] = "Barrier: Signals Only", sections The idea
+ * and Walkthrough).  Every rank owns a signal window of P int32 cells, one
+ * row per rank, and cell s of a window is written by rank s alone, so no two
+ * ranks ever update the same word.  W holds the P windows stacked: W[q*P + s]
+ * is the cell of row s in rank q's window.  The cells only grow ([BAR] Edge
+ * cases): generation g of a rendezvous waits for >= g instead of resetting.
+ * Every collective lowers to these two calls: notify the peers, then wait
+ * for the rows one expects.
+ */
+
+/* notify: rank `me` adds 1 to its own row's cell in rank `peer`'s window,
+ * W[peer][me] += 1, as a release at system scope: stores this wave made
+ * before the call are visible to any thread that sees the new count.  To
+ * publish a whole CTA's stores, every wave first waits for its own stores
+ * (s_waitcnt vmcnt(0)) and the CTA syncs, as in mark_ready.  Per lane: each
+ * calling lane notifies the peer it names, so one wave can notify every peer
+ * at once (lane q notifying rank q); a lane naming peer >= P or peer == me
+ * does nothing. */
+__device__ inline void tc_notify(int32_t* W, uint32_t P, uint32_t me, uint32_t peer) {
+  if (peer < P && peer != me)
+    __hip_atomic_fetch_add(W + (uint64_t)peer * P + me, 1, __ATOMIC_RELEASE,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+/* wait_ge: rank `me` waits until row `src` of its own window holds at least
+ * `expected`, W[me][src] >= expected.  Whole wave, wave-uniform result.  Each
+ * lane names its own src, so one wave can wait on every row at once (lane s
+ * on row s); a lane naming src >= P or src == me waits for nothing.  Polls
+ * are relaxed and counted (at most max_polls + 1, never a clock); the wave
+ * leaves the loop together on a vote once every lane's cell is high enough,
+ * then acquires at system scope, so whatever a notifier released before its
+ * notify is visible afterwards.  Returns false when the polls ran out. */
+__device__ inline bool tc_wait_ge(const int32_t* W, uint32_t P, uint32_t me, uint32_t src,
+                                  int32_t expected, uint32_t max_polls) {
+  const bool mine = src < P && src != me;
+  const int32_t* cell = W + (uint64_t)me * P + (mine ? src : 0u);
+  for (uint32_t polls = 0;; ++polls) {
+    bool ok = true;
+    if (mine)
+      ok = __hip_atomic_load(cell, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) >= expected;
+    if (__all(ok)) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");  // system-scope acquire
+      return true;
+    }
+    if (polls >= max_polls) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
 /* The producer's step->tile map: group_m tile-rows walked column by column,
  * then the next band of rows (the grouped order [TP] Model's tile_of stands
  * for).  Plain integer arithmetic, shared by host and device so the schedule

@@ -20,6 +20,7 @@ the notation of the pages it follows:
 Modules
 -------
 ``values``    seeded value hash the synthetic producers write (SplitMix64 mix).
+``cvalues``   the same hash in plain C (``values.c``), for full-size checks.
 ``schedule``  views -> regions -> chunks; ``whole``/``chunks``/``tile_chunks``;
               grouped step->tile order; plan-creation validation.
 ``plan``      the step-by-step simulation of gates, in-order queues and rounds.

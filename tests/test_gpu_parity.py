@@ -221,6 +221,93 @@ def test_plan_queued_behind_another_is_closing():
         pair.close()
 
 
+@pytest.mark.parametrize("rounds_before", [0, 1])
+def test_close_before_start_sends_chunks_as_they_stand(rounds_before):
+    # [TP] The kernel author's contract: closing a plan before its round
+    # starts still sends each rank's chunks as they stand.  The producer
+    # writes the round's data into a READY plan (no start, no marks); close()
+    # must deliver it everywhere, as a full round of the oracle does.
+    w = dict(workloads.SMALL["u32_chunks_ragged_p3"])
+    pair = Pair(w)
+    try:
+        for r in range(1, rounds_before + 1):
+            pair.gpu_round_fill()
+            pair.oracle_round()
+            pair.compare(f"close-before-start warm-up round {r}")
+            pair.plan.next_round()
+            pair.sim.next_round()
+        h = pair.plan.current_handle()
+        pair.plan.fill(h, pair.tv, pair.seed, kind="u32", mark=False, stream=pair.stream)
+        pair.stream.synchronize()
+        assert pair.plan.state == "READY"
+        log(f"close before start, round {rounds_before + 1}")
+        assert pair.plan.close() == "CLOSED"
+        want = _expected_replicas(pair, rounds_before + 1)
+        host = pair.rep.cpu().numpy()
+        for q in range(pair.P):
+            assert np.array_equal(host[q], want[q]), f"replica {q} after close before start"
+    finally:
+        pair.close()
+
+
+def test_plan_behind_a_slow_unblocked_plan_closes_closed():
+    # A's gates are all open but its engine is slow (one CTA, 256-byte
+    # pieces); B's round is queued behind it on the shared engine stream.
+    # B is not behind *waiting* copies, so close() must wait for A's engine
+    # and then free B (CLOSED, not CLOSING), with B's round delivered.
+    wa = dict(P=2, rows=2048, cols=16384, elem="u32", builder="whole", writers=4, rounds=1)
+    wb = dict(P=3, rows=24, cols=40, elem="u32", builder="chunks", n=3, writers=1, rounds=1)
+    a = Pair(wa, oracle_bytes=False, engine_ctas=1, piece_bytes=256)
+    b = Pair(wb, seed=BASE_SEED + 5)
+    try:
+        ha = a.plan.start(a.stream)
+        a.plan.fill(ha, a.tv, a.seed, kind="u32", mark=True, stream=a.stream)
+        hb = b.plan.start(a.stream)
+        b.plan.fill(hb, b.tv, b.seed, kind="u32", mark=True, stream=a.stream)
+        a.stream.synchronize()
+        import time
+        t0 = time.perf_counter()
+        assert b.plan.close() == "CLOSED"
+        log(f"close() behind a slow unblocked plan returned after {time.perf_counter() - t0:.3f} s")
+        a.plan.wait(30.0)
+        log(f"the slow plan's engine took {a.plan.stats()['engine_ms']:.1f} ms")
+        a.oracle_round()
+        a.compare("slow plan")
+        want = _expected_replicas(b, 1)
+        host = b.rep.cpu().numpy()
+        for q in range(b.P):
+            assert np.array_equal(host[q], want[q]), f"replica {q} of the closed plan"
+    finally:
+        b.close()
+        a.close()
+
+
+def test_wait_deadline_while_producer_runs_still_counts_its_marks():
+    # wait() waits on the host for the producer's stream until its deadline;
+    # past it, the completion check is queued behind the producer on the
+    # device.  A deadline far shorter than a slow producer (one CTA writing
+    # every rank's block), followed by an extra mark queued on the same
+    # stream, must still report that mark (EEXTRA, plan FAILED): the check
+    # runs only after the producer's work.  The engine is stopped from the
+    # host at the deadline, so every kernel exits normally.
+    w = dict(P=4, rows=1024, cols=16384, elem="u32", builder="chunks", n=4, writers=2, rounds=1)
+    pair = Pair(w, oracle_bytes=False)
+    try:
+        h = pair.plan.start(pair.stream)
+        pair.plan.fill(h, pair.tv, pair.seed, kind="u32", waves=True, ctas=1, stream=pair.stream)
+        pair.plan.mark(h, 2, 1, 1, stream=pair.stream)
+        with pytest.raises(tc.ExtraMarksError) as ei:
+            pair.plan.wait(0.001)
+        assert ei.value.chunks == [(2, 1)]
+        assert pair.plan.state == "FAILED"
+        pair.stream.synchronize()
+        with pytest.raises(oplan.PlanError) as eo:
+            pair.oracle_round(extra=[(2, 1)])
+        assert eo.value.chunks == [(2, 1)]
+    finally:
+        pair.close()
+
+
 def test_nested_plans_in_with_blocks():
     # Two plans as nested context managers over separate buffers ([TP]
     # Model: a plan is a context manager; leaving the block closes it).  A

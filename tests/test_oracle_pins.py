@@ -14,7 +14,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle import barrier, gemm, plan, schedule, values
+from oracle import barrier, cvalues, gemm, plan, schedule, values
 from oracle.schedule import GIB, View
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -38,6 +38,29 @@ def test_splitmix64_published_vector():
     assert values.splitmix64_stream(1234567, 5) == [
         6457827717110365317, 3203168211198807973, 9817491932198370423,
         4593380528125082431, 16408922859458223821]
+
+
+def test_c_twin_reproduces_the_published_vector():
+    # The oracle's C twin of the value hash (oracle/values.c), used to check
+    # every element of the largest workloads, pinned to the same published
+    # splitmix64.c output for seed 1234567.
+    assert cvalues.splitmix64_stream(1234567, 5) == [
+        6457827717110365317, 3203168211198807973, 9817491932198370423,
+        4593380528125082431, 16408922859458223821]
+
+
+@pytest.mark.parametrize("rank,rnd,first,n,nthreads", [(0, 1, 0, 4099, 1), (3, 2, (1 << 32) - 5000, 5000, 7),
+                                                        (15, 65535, 123456789, 100003, 16)])
+def test_c_twin_pattern_equals_the_numpy_oracle(rank, rnd, first, n, nthreads):
+    # Element by element, across thread splits and at the top of the index
+    # range; a wrong key layout (rank or round in the wrong bits) or a
+    # dropped salt fails here.
+    out = np.zeros(n, dtype=np.uint32)
+    cvalues.u32_pattern_into(out, 0x7C0FFEE, rank, rnd, first, nthreads=nthreads)
+    want = values.u32_pattern(0x7C0FFEE, rank, rnd, np.arange(first, first + n, dtype=np.uint64))
+    assert np.array_equal(out, want)
+    with pytest.raises(ValueError):
+        cvalues.u32_pattern_into(np.zeros(2, dtype=np.uint32), 1, 1 << 16, 0, 0)
 
 
 def test_mix64_vectorised_matches_scalar():

@@ -10,7 +10,9 @@ SDMA Plans" (Iris pull request) -- API; "Barrier: Signals Only" (pypto
 documentation) -- Walkthrough.
 """
 
+import atexit
 import ctypes as C
+import weakref
 
 import numpy as np
 
@@ -21,7 +23,7 @@ from ._lib import (FILL_BF16, FILL_U8, FILL_U32, MARK_INKERNEL, MARK_NONE,  # no
 
 __all__ = ["View", "Schedule", "whole", "chunks", "tile_chunks", "from_arrays", "order_grouped",
            "view_of", "TriggeredPlan", "prepare_all_gather", "gemm_bf16", "gemm_consume_bf16",
-           "barrier",
+           "barrier", "release",
            "TriggeredCopyError",
            "PlanTimeout", "ExtraMarksError", "StateError", "RoundLimitError"]
 
@@ -89,6 +91,35 @@ _ERRORS = {c.code: c for c in (InvalidArgument, BoundsError, OverlapError, Works
 
 def lib():
     return _lib.load()
+
+
+# Plans not yet closed.  At interpreter exit they are closed and the
+# library's process-lifetime engine streams are released, while the HIP
+# runtime is still whole: freeing them from finalizers during the runtime's
+# own teardown is not safe.
+_LIVE = weakref.WeakSet()
+
+
+@atexit.register
+def _close_all_at_exit():
+    if _lib._lib is None:
+        return
+    for _ in range(3):                   # a CLOSING plan finishes once the plan before it closes
+        for plan in list(_LIVE):
+            try:
+                plan.close()
+            except Exception:
+                pass
+        if not _LIVE:
+            break
+    if not _LIVE:
+        _lib._lib.tc_release()
+
+
+def release():
+    """Destroys the library's cached engine streams (tc_release).  Every
+    plan must be closed first."""
+    _check(lib().tc_release())
 
 
 def _check(rc, chunks=()):
@@ -287,6 +318,7 @@ class TriggeredPlan:
             _check(lib().tc_plan_create(C.byref(d), C.byref(ptr)))
         self._p = ptr
         self.handle = None
+        _LIVE.add(self)
 
     # -- context manager
     def __enter__(self):
@@ -309,6 +341,7 @@ class TriggeredPlan:
             return "CLOSING"
         if rc == _lib.OK:
             self._p = C.c_void_p(0)
+            _LIVE.discard(self)
         _check(rc)
         return "CLOSED"
 

@@ -94,7 +94,7 @@ _SIGS = {
     "tc_barrier_run": [vp, u32, u32, u32, vp, vp, vp, u32, vp, vp],
 }
 
-EXPORTS = sorted(list(_SIGS) + ["tc_schedule_free", "tc_last_error", "tc_version"])
+EXPORTS = sorted(list(_SIGS) + ["tc_schedule_free", "tc_last_error", "tc_version", "tc_release"])
 
 _lib = None
 
@@ -119,5 +119,7 @@ def load() -> C.CDLL:
     lib.tc_last_error.restype = C.c_char_p
     lib.tc_version.argtypes = []
     lib.tc_version.restype = C.c_char_p
+    lib.tc_release.argtypes = []
+    lib.tc_release.restype = C.c_int
     _lib = lib
     return lib

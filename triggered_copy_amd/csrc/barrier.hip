@@ -9,15 +9,17 @@
 //
 // The P windows are stacked as W[P][P] int32; W[q][s] is the cell of row s in
 // rank q's window, written only by rank s.  One 64-lane wave per simulated
-// rank: lane q notifies rank q (release), lane s polls row s (relaxed reads,
-// then one acquire fence once every lane has seen its threshold, decided by a
-// wave vote so the whole wave leaves the loop together).  Polls are counted
-// and bounded, so every wave exits even if a peer never arrives.
+// rank, built on the device calls of tc_device.h: lane q notifies rank q
+// (tc_notify, a release add), and the wave waits with lane s on row s
+// (tc_wait_ge: relaxed polls, a wave vote so the whole wave leaves the loop
+// together, then one acquire).  Polls are counted and bounded, so every wave
+// exits even if a peer never arrives.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
 #include "plan_internal.h"
 #include "tc.h"
+#include "tc_device.h"
 
 using tc::fail;
 
@@ -40,22 +42,8 @@ __global__ __launch_bounds__(64) void barrier_kernel(BarrierArgs a) {
     const uint32_t g = a.first_gen + i;
     if (a.x && lane == 0) a.x[(g & 1) * P + m] = (int32_t)((g << 8) | m);  // stage
     __syncthreads();
-    if (lane < P && lane != m)
-      __hip_atomic_fetch_add(a.W + lane * P + m, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
-    bool ok = true;
-    for (uint32_t polls = 0;; ++polls) {
-      bool mine = true;
-      if (lane < P && lane != m)
-        mine = __hip_atomic_load(a.W + m * P + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) >=
-               (int32_t)g;
-      if (__all(mine)) break;
-      if (polls >= a.max_polls) {
-        ok = false;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-    if (!ok) {
+    tc_notify(a.W, P, m, lane);  // lane q notifies rank q
+    if (!tc_wait_ge(a.W, P, m, lane, (int32_t)g, a.max_polls)) {  // lane s waits on row s
       if (lane == 0) {
         uint32_t expected = 0;
         __hip_atomic_compare_exchange_strong(a.status, &expected, 1 + m, __ATOMIC_RELAXED,
@@ -63,7 +51,6 @@ __global__ __launch_bounds__(64) void barrier_kernel(BarrierArgs a) {
       }
       return;
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
     if (a.snap && lane < P)
       a.snap[((uint64_t)i * P + m) * P + lane] =
           __hip_atomic_load(a.W + m * P + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);

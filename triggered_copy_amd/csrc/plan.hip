@@ -141,7 +141,7 @@ struct EngineArgs {
   uint32_t round;
   uint32_t nranks;
   uint32_t launch_id;
-  uint32_t pad;
+  uint32_t nchunks;       // G
   uint64_t backstop_ticks;
 };
 
@@ -348,6 +348,56 @@ __device__ void copy_2d(const EngineArgs& a, uint32_t p, const PieceD& pc) {
   }
 }
 
+// The sum of global chunk g's mark stripes, per lane (each lane its own g).
+__device__ inline uint64_t lane_mark_count(const EngineArgs& a, uint32_t g) {
+  const uint64_t* s = reinterpret_cast<const uint64_t*>(a.marks + (uint64_t)g * TC_MARK_STRIPES *
+                                                                       TC_MARK_STRIPE_BYTES);
+  uint64_t sum = 0;
+#pragma unroll
+  for (uint32_t k = 0; k < TC_MARK_STRIPES; ++k)
+    sum += __hip_atomic_load(s + k * (TC_MARK_STRIPE_BYTES / 8), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  return sum;
+}
+
+// The gate publisher: one wave of the engine stands in for the pages' last
+// writer, whose increment returns the count and who then stores the round
+// into the gate's `ready` word ([TP] Memory ordering).  Marks here add to
+// striped counters without learning the total, so this wave watches every
+// chunk's stripes (lane i takes chunks i, i + 64, ...) and stores the round
+// into `ready`, in the sender's own gate row, once the count reaches
+// round * writers.  It does this for every chunk as its marks complete,
+// whatever the copy queues are doing (a chunk held back behind a shut
+// earlier chunk still shows its gate open), and leaves once every gate of
+// the round is published, or when close() forces the gates open, or when
+// the launch must stop.  The copy waves poll the stripes themselves, so
+// the publisher is never on a copy's critical path; the engine's exit, and
+// so the completion check, come after every `ready` store.
+__device__ void publish_gates(const EngineArgs& a, uint64_t t0) {
+  const uint32_t lane = tc_lane_id();
+  for (uint32_t spins = 0;;) {
+    uint32_t shut = 0;
+    for (uint32_t base = 0; base < a.nchunks; base += 64) {
+      const uint32_t g = base + lane;
+      if (g < a.nchunks) {
+        const ChunkD cd = a.chunks[g];
+        uint64_t* ready = &gate_row(a, cd.rank, g)->ready;
+        if (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) < a.round) {
+          if (lane_mark_count(a, g) >= (uint64_t)a.round * cd.writers)
+            __hip_atomic_store(ready, (uint64_t)a.round, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          else
+            shut = 1;
+        }
+      }
+    }
+    if (__all(shut == 0)) return;
+    if (wave_load_sys(a.force) != 0) return;
+    if (must_stop(a, t0, ++spins)) return;
+    if (spins < 256) __builtin_amdgcn_s_sleep(2);
+    else __builtin_amdgcn_s_sleep(32);
+  }
+}
+
 // The copy engine.  Every wave is an independent worker; all control flow is
 // wave-uniform (no per-lane branch in any loop), so no lane can be left
 // behind in a loop its wave has to leave together.
@@ -364,6 +414,10 @@ __global__ __launch_bounds__(kEngineThreads) void engine_kernel(EngineArgs a) {
     a.zero_round[i] = 0;
 
   const uint64_t t0 = now_ticks();
+  if (gw == 0) {  // global wave 0 publishes the gates' `ready` words and copies nothing
+    publish_gates(a, t0);
+    return;
+  }
   uint32_t acquired = 0xFFFFFFFFu;  // last chunk whose gate this wave has seen open
   // Large grids keep one wave in eight polling briskly and let the rest back
   // off; small grids poll with every wave.
@@ -445,12 +499,17 @@ __device__ uint32_t check_chunk(const CheckArgs& a, uint32_t g) {
         a.gates + (uint64_t)q * a.gate_stride + (uint64_t)g * TC_GATE_ROW_BYTES);
     for (int k = 0; k < 5; ++k)
       if (ld(&r->rsvd[k]) != 0) f |= kFlagCorrupt;
-    if (ld(&r->ready) != 0 || ld(&r->writers) != 0) f |= kFlagCorrupt;
+    if (ld(&r->writers) != 0) f |= kFlagCorrupt;
     const uint64_t arr = ld(&r->arrival);
+    const uint64_t rdy = ld(&r->ready);
     if (q == cd.rank) {
-      if (arr != 0) f |= kFlagCorrupt;
+      // The sender's row: no arrival; `ready` is this round once the gate
+      // has opened (it is stored before the chunk is signalled anywhere).
+      if (arr != 0 || rdy > a.round) f |= kFlagCorrupt;
+      if (rdy < a.round) f |= kFlagNotArrived;
       continue;
     }
+    if (rdy != 0) f |= kFlagCorrupt;
     if (arr < a.round) f |= kFlagNotArrived;
     if (arr > a.round) f |= kFlagCorrupt;
   }
@@ -488,23 +547,38 @@ int hip_fail(hipError_t e, const char* what) {
   } while (0)
 
 // Engine streams are shared by every plan on the same device with the same
-// CU mask and live until the process ends: each one owns a hardware queue
-// (and its wave save area), which are too costly to create per plan.  Plans
-// that share a stream run their engines in the order they were started.
+// CU mask: each one owns a hardware queue (and its wave save area), which
+// are too costly to create per plan.  Plans that share a stream run their
+// engines in the order they were started.  The registry also lists the live
+// plans, so that close() can tell whether a plan's launch is queued behind
+// another plan's waiting engine, and tc_release() can destroy the streams
+// once no plan is left.  It is never destroyed itself, so nothing of it runs
+// in the process's exit-time destructors.
+struct Registry {
+  std::mutex mu;
+  std::map<std::pair<int, std::vector<uint32_t>>, hipStream_t> streams;
+  std::vector<tc_plan*> live;
+  uint64_t submits = 0;  // engine launches so far, in submission order
+};
+
+static Registry& registry() {
+  static Registry* r = new Registry();
+  return *r;
+}
+
 static int engine_stream_for(int device, const std::vector<uint32_t>& mask, hipStream_t* out) {
-  static std::mutex mu;
-  static std::map<std::pair<int, std::vector<uint32_t>>, hipStream_t> streams;
-  std::lock_guard<std::mutex> lock(mu);
+  Registry& R = registry();
+  std::lock_guard<std::mutex> lock(R.mu);
   auto key = std::make_pair(device, mask);
-  auto it = streams.find(key);
-  if (it != streams.end()) {
+  auto it = R.streams.find(key);
+  if (it != R.streams.end()) {
     *out = it->second;
     return TC_OK;
   }
   hipStream_t s = nullptr;
   const hipError_t e = hipExtStreamCreateWithCUMask(&s, (uint32_t)mask.size(), mask.data());
   if (e != hipSuccess) return hip_fail(e, "hipExtStreamCreateWithCUMask (engine stream)");
-  streams.emplace(key, s);
+  R.streams.emplace(key, s);
   *out = s;
   return TC_OK;
 }
@@ -547,6 +621,7 @@ static int launch_engine(tc_plan* P) {
   for (uint32_t p = 0; p <= P->P; ++p) a.piece_base[p] = P->piece_base[p];
   a.round = P->round;
   a.nranks = P->P;
+  a.nchunks = P->G;
   a.launch_id = ++P->launch_id;
   a.backstop_ticks = P->backstop_ticks;
   P->cur_launch_block = lb;
@@ -557,7 +632,13 @@ static int launch_engine(tc_plan* P) {
     P->engine_ms_pending = false;
   }
   TC_HIP(hipEventRecord(P->ev_engine_start, P->engine_stream));
-  hipLaunchKernelGGL(engine_kernel, dim3(P->engine_ctas), dim3(kEngineThreads), 0, P->engine_stream, a);
+  {
+    Registry& R = registry();
+    std::lock_guard<std::mutex> lock(R.mu);
+    hipLaunchKernelGGL(engine_kernel, dim3(P->engine_ctas), dim3(kEngineThreads), 0, P->engine_stream,
+                       a);
+    P->last_submit = ++R.submits;
+  }
   TC_HIP(hipGetLastError());
   TC_HIP(hipEventRecord(P->ev_engine_done, P->engine_stream));
   P->launches_this_round++;
@@ -629,6 +710,52 @@ static int check_done_by(const tc_plan* P, uint32_t seq,
   }
 }
 
+// Whether every gate of plan Q is open in its current round (or forced
+// open by close()), from its mark stripes read now.
+static int gates_all_open(tc_plan* Q, bool* open) {
+  *open = true;
+  if (Q->forced || Q->G == 0) return TC_OK;
+  std::vector<uint64_t> marks((size_t)Q->G * TC_MARK_STRIPES * (TC_MARK_STRIPE_BYTES / 8));
+  TC_HIP(hipMemcpyAsync(marks.data(), Q->ws + Q->L.marks, marks.size() * 8, hipMemcpyDeviceToHost,
+                        Q->aux_stream));
+  TC_HIP(hipStreamSynchronize(Q->aux_stream));
+  for (uint32_t g = 0; g < Q->G; ++g) {
+    uint64_t count = 0;
+    for (uint32_t k = 0; k < TC_MARK_STRIPES; ++k)
+      count += marks[((size_t)g * TC_MARK_STRIPES + k) * (TC_MARK_STRIPE_BYTES / 8)];
+    if (count < (uint64_t)Q->round * Q->chunks[g].writers) {
+      *open = false;
+      return TC_OK;
+    }
+  }
+  return TC_OK;
+}
+
+// Whether P's newest engine launch is queued behind an earlier launch on
+// the same stream that cannot finish by itself: a plan whose engine has not
+// finished and some of whose gates are shut and not forced.  Plans behind
+// such a plan are caught too, since their launches are earlier than P's.
+static int queued_behind_blocked_plan(tc_plan* P, bool* blocked) {
+  *blocked = false;
+  Registry& R = registry();
+  std::lock_guard<std::mutex> lock(R.mu);
+  for (tc_plan* Q : R.live) {
+    if (Q == P || Q->engine_stream != P->engine_stream || Q->last_submit == 0 ||
+        Q->last_submit > P->last_submit)
+      continue;
+    const hipError_t e = hipEventQuery(Q->ev_engine_done);
+    if (e == hipSuccess) continue;
+    if (e != hipErrorNotReady) return hip_fail(e, "close: hipEventQuery (earlier plan)");
+    bool open = true;
+    if (int rc = gates_all_open(Q, &open)) return rc;
+    if (!open) {
+      *blocked = true;
+      return TC_OK;
+    }
+  }
+  return TC_OK;
+}
+
 }  // namespace tc
 
 using namespace tc;
@@ -669,6 +796,11 @@ int tc_plan_validate(const tc_plan_desc* d) {
 
 static void destroy(tc_plan* P) {
   if (!P) return;
+  {
+    Registry& R = registry();
+    std::lock_guard<std::mutex> lock(R.mu);
+    R.live.erase(std::remove(R.live.begin(), R.live.end(), P), R.live.end());
+  }
   if (P->aux_stream) (void)hipStreamDestroy(P->aux_stream);
   for (hipEvent_t e : {P->ev_prod_start, P->ev_prod_end, P->ev_engine_start, P->ev_engine_done,
                        P->ev_check_done})
@@ -859,7 +991,8 @@ int tc_plan_create(const tc_plan_desc* d, tc_plan** out) {
   // 192 KiB of delivered bytes per round, at most 16 per usable CU (the count
   // that saturates HBM).  A wave's work is what it writes: each piece it
   // reads goes to all P - 1 receivers.  Fewer waves leave the producer's CUs
-  // quieter when a round moves little data.
+  // quieter when a round moves little data.  One more wave is the gate
+  // publisher, which copies nothing.
   const uint32_t npieces = (uint32_t)P->pieces.size();
   uint64_t src_bytes = 0;
   for (const ChunkD& c : P->chunks) src_bytes += c.bytes;
@@ -868,10 +1001,12 @@ int tc_plan_create(const tc_plan_desc* d, tc_plan** out) {
     P->engine_ctas = d->engine_ctas;
   } else {
     const uint64_t waves = std::min<uint64_t>(
-        16ull * usable, std::max<uint64_t>(std::min<uint64_t>(npieces, 256), delivered / (192u << 10)));
+        16ull * usable,
+        std::max<uint64_t>(std::min<uint64_t>(npieces, 256) + 1, delivered / (192u << 10)));
     P->engine_ctas = (uint32_t)((waves + 3) / 4);
   }
-  P->engine_ctas = std::max<uint32_t>(1, std::min<uint32_t>(P->engine_ctas, (std::max<uint32_t>(npieces, 1) + 3) / 4));
+  P->engine_ctas = std::max<uint32_t>(
+      1, std::min<uint32_t>(P->engine_ctas, (std::max<uint32_t>(npieces, 1) + 1 + 3) / 4));
   const uint64_t backstop_us = d->engine_backstop_us ? d->engine_backstop_us : 30ull * 1000 * 1000;
   P->backstop_ticks = backstop_us * 100;  // s_memrealtime runs at 100 MHz
   for (const ChunkD& c : P->chunks) {
@@ -881,6 +1016,11 @@ int tc_plan_create(const tc_plan_desc* d, tc_plan** out) {
   P->round = 1;
   P->state = TC_STATE_READY;
 #undef TC_HIP_C
+  {
+    Registry& R = registry();
+    std::lock_guard<std::mutex> lock(R.mu);
+    R.live.push_back(P);
+  }
   *out = P;
   return TC_OK;
 }
@@ -920,15 +1060,24 @@ int tc_plan_wait(tc_plan* P, uint64_t timeout_us) {
   // device-side dependency on the other stream starts it about 4 us later.
   // Past the deadline the dependency is put on the device after all.  The
   // queries are spaced 2 us apart: back to back, they slowed the kernels
-  // running meanwhile (GEMM producers beside the engine) by about 2%.
-  for (;;) {
-    const hipError_t q = hipStreamQuery(P->producer_stream);
-    if (q == hipSuccess) break;
-    if (q != hipErrorNotReady) return hip_fail(q, "hipStreamQuery(producer stream)");
-    const auto now = std::chrono::steady_clock::now();
-    if (now >= deadline) break;
-    const auto next = now + std::chrono::microseconds(2);
-    while (std::chrono::steady_clock::now() < next) {
+  // running meanwhile (GEMM producers beside the engine) by about 2%.  After
+  // 1 ms the host sleeps 20 us between queries instead of spinning, so a long
+  // producer does not hold a host core for the whole round.
+  {
+    const auto spin_until = std::chrono::steady_clock::now() + std::chrono::milliseconds(1);
+    for (;;) {
+      const hipError_t q = hipStreamQuery(P->producer_stream);
+      if (q == hipSuccess) break;
+      if (q != hipErrorNotReady) return hip_fail(q, "hipStreamQuery(producer stream)");
+      const auto now = std::chrono::steady_clock::now();
+      if (now >= deadline) break;
+      if (now >= spin_until) {
+        std::this_thread::sleep_for(std::chrono::microseconds(20));
+        continue;
+      }
+      const auto next = now + std::chrono::microseconds(2);
+      while (std::chrono::steady_clock::now() < next) {
+      }
     }
   }
   if (int rc = queue_check(P)) return rc;
@@ -1005,31 +1154,53 @@ int tc_plan_close(tc_plan* P, int* closing) {
   if (!P) return TC_OK;
   const auto deadline = [](int s) { return std::chrono::steady_clock::now() + std::chrono::seconds(s); };
   hipError_t err = hipSuccess;
-  const bool mid_round = P->state == TC_STATE_STARTED || P->state == TC_STATE_CLOSING;
-  if (mid_round && !P->forced) {
-    // Send every chunk as it stands ([TP] The kernel author's contract:
-    // closing mid-round): force every gate open, and run the engine again if
-    // a timeout stopped it.
+  // Prepared copies are sent as the chunks stand ([TP] The kernel author's
+  // contract: closing in the middle of a round, or before it starts): force
+  // every gate of the plan open, and run the engine -- for a round prepared
+  // but not started, or again when a timeout stopped it.  A DONE or FAILED
+  // round has nothing left to send.
+  const bool sends = P->state == TC_STATE_STARTED || P->state == TC_STATE_CLOSING ||
+                     P->state == TC_STATE_READY;
+  if (sends && !P->forced) {
     const uint32_t one = 1;
     TC_HIP(hipMemcpyAsync(P->ws + P->L.status + kForceOffset, &one, 4, hipMemcpyHostToDevice,
                           P->aux_stream));
     TC_HIP(hipStreamSynchronize(P->aux_stream));
     P->forced = true;
-    if (P->need_relaunch) {
+    if (P->state == TC_STATE_READY || P->need_relaunch) {
+      if (P->state == TC_STATE_READY) {
+        P->launches_this_round = 0;
+        P->problems.clear();
+      }
       if (int rc = launch_engine(P)) return rc;
       P->need_relaunch = false;
     }
   }
   if (P->launch_id) {
-    // The engine stream may be shared with other plans: this plan's launch
-    // may still be queued behind another plan's engine, which waits for that
-    // plan's gates.  Then the plan stays CLOSING; closing the earlier plan
-    // lets this one finish, and a later close() frees it.
-    // (A launch just submitted needs a moment to start: give it one second.)
-    if (closing && event_done_by(P->ev_engine_start, deadline(1), &err) == 0) {
-      P->state = TC_STATE_CLOSING;
-      *closing = 1;
-      return TC_OK;
+    if (closing) {
+      // The engine stream may be shared with other plans, so this plan's
+      // launch may be queued behind another plan's engine.  As long as that
+      // engine can finish by itself (its gates are open, or forced), wait
+      // for it; once it is waiting on shut gates, this plan cannot finish
+      // first ([TP] The kernel author's contract): it stays CLOSING, and a
+      // later close() frees it after the earlier plan is closed.
+      const auto until = deadline(10);
+      for (;;) {
+        const hipError_t e = hipEventQuery(P->ev_engine_done);
+        if (e == hipSuccess) break;
+        if (e != hipErrorNotReady) return hip_fail(e, "close: hipEventQuery");
+        if (hipEventQuery(P->ev_engine_start) != hipSuccess) {
+          bool blocked = false;
+          if (int rc = queued_behind_blocked_plan(P, &blocked)) return rc;
+          if (blocked) {
+            P->state = TC_STATE_CLOSING;
+            *closing = 1;
+            return TC_OK;
+          }
+        }
+        if (std::chrono::steady_clock::now() >= until) break;
+        std::this_thread::sleep_for(std::chrono::microseconds(100));
+      }
     }
     int done = event_done_by(P->ev_engine_done, deadline(10), &err);
     if (done != 1) {  // the forced engine did not finish: stop it
@@ -1043,6 +1214,20 @@ int tc_plan_close(tc_plan* P, int* closing) {
   }
   destroy(P);
   return TC_OK;
+}
+
+int tc_release(void) {
+  Registry& R = registry();
+  std::lock_guard<std::mutex> lock(R.mu);
+  if (!R.live.empty())
+    return fail(TC_ESTATE, "release: " + std::to_string(R.live.size()) + " plan(s) still open");
+  int rc = TC_OK;
+  for (auto& kv : R.streams) {
+    const hipError_t e = hipStreamDestroy(kv.second);
+    if (e != hipSuccess && rc == TC_OK) rc = hip_fail(e, "release: hipStreamDestroy (engine stream)");
+  }
+  R.streams.clear();
+  return rc;
 }
 
 int tc_plan_state(const tc_plan* P, int* state, uint32_t* round) {
@@ -1077,8 +1262,9 @@ int tc_plan_read_gates(tc_plan* P, void* host, uint64_t bytes) {
   TC_HIP(hipMemcpyAsync(marks.data(), P->ws + P->L.marks, marks.size() * 8, hipMemcpyDeviceToHost,
                         P->aux_stream));
   TC_HIP(hipStreamSynchronize(P->aux_stream));
-  // The sender's row: writers = the stripes' sum, ready = the last round
-  // whose gate that count opened (at most the current round).
+  // The sender's row: `ready` and `arrival` are the device words as read;
+  // the writer counter is kept striped on the device, and its value is the
+  // stripes' sum.
   for (uint32_t g = 0; g < P->G; ++g) {
     const ChunkD& cd = P->chunks[g];
     uint64_t count = 0;
@@ -1087,7 +1273,6 @@ int tc_plan_read_gates(tc_plan* P, void* host, uint64_t bytes) {
     auto* row = reinterpret_cast<tc_gate_row*>((uint8_t*)host +
                                                ((uint64_t)cd.rank * P->G + g) * TC_GATE_ROW_BYTES);
     row->writers = count;
-    row->ready = std::min<uint64_t>(count / cd.writers, P->round);
   }
   return TC_OK;
 }

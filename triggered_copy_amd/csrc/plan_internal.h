@@ -76,6 +76,7 @@ struct tc_plan {
   uint32_t round = 1;
   int state = TC_STATE_READY;
   uint32_t launch_id = 0;    // id of the newest engine launch (abort compares to it)
+  uint64_t last_submit = 0;  // process-wide submission number of the newest engine launch
   uint32_t launch_seq = 0;   // launches so far; parity picks the launch block
   uint32_t cur_launch_block = 0;
   uint32_t launches_this_round = 0;
