@@ -543,6 +543,8 @@ def main():
                     help="also run an elementwise kernel reading and writing 1 GiB each, "
                          "the reference for scaling HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--overlap-only", action="store_true",
+                    help="time only the GEMM producers with and without the copy engine")
     ap.add_argument("--small-round", default=None, metavar="WORKLOAD",
                     help="time only full rounds (start, fill with in-kernel marks, wait) of a small "
                          "workload, --steps rounds (for per-kernel traces and counters)")
@@ -560,6 +562,10 @@ def main():
     tc.lib()
     if args.gemm_only:
         print(json.dumps(run_gemm_only(torch, tc, workloads, BASE_SEED, args.steps)), flush=True)
+        return
+    if args.overlap_only:
+        print(json.dumps(run_overlap(torch, tc, workloads, BASE_SEED,
+                                     engine_ctas=args.overlap_engine_ctas)), flush=True)
         return
 
     if args.calibrate:

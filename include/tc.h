@@ -212,7 +212,7 @@ typedef struct tc_plan_desc {
   uint64_t rows_per_rank_bytes;        /* for TC_CHECK_OWN_ROWS */
   const uint32_t* cu_mask;             /* NULL = copy engine may use every CU */
   uint32_t cu_mask_words;
-  uint32_t engine_ctas;                /* CTAs of 4 waves (wave 0 of the grid publishes the
+  uint32_t engine_ctas;                /* CTAs of 4 waves (the grid's last wave publishes the
                                           gates, the others copy); 0 = one wave per 192 KiB of
                                           delivered bytes per round (source bytes times the
                                           P - 1 receivers), at least one per piece up to 256

@@ -288,9 +288,9 @@ class TriggeredPlan:
         self._keep = (reps, list(schedules))
         sched_ptrs = (C.c_void_p * P)(*[s.ptr.value if s is not None else None for s in schedules])
         self._sched_ptrs = sched_ptrs
-        ws_need = C.c_uint64()
-        _check(lib().tc_plan_workspace_bytes(P, sched_ptrs, piece_bytes, C.byref(ws_need)))
         if workspace is None:
+            ws_need = C.c_uint64()
+            _check(lib().tc_plan_workspace_bytes(P, sched_ptrs, piece_bytes, C.byref(ws_need)))
             workspace = torch.empty(ws_need.value, dtype=torch.uint8, device=reps[0].device)
         self.workspace = workspace
         rep_ptrs = (C.c_void_p * P)(*[r.data_ptr() for r in reps])
@@ -301,8 +301,8 @@ class TriggeredPlan:
         d.replicas = C.cast(rep_ptrs, C.POINTER(C.c_void_p))
         d.buffer_bytes = nbytes
         d.schedules = C.cast(sched_ptrs, C.POINTER(C.c_void_p))
-        d.workspace = workspace.data_ptr()
-        d.workspace_bytes = workspace.numel()
+        d.workspace = workspace.data_ptr() if workspace is not None else None
+        d.workspace_bytes = workspace.numel() if workspace is not None else 0
         d.rows_per_rank_bytes = own_rows_bytes or 0
         if cu_mask is not None:
             m = (C.c_uint32 * len(cu_mask))(*cu_mask)
@@ -314,8 +314,9 @@ class TriggeredPlan:
         d.engine_backstop_us = int(backstop_s * 1e6)
         self._desc = d
         ptr = C.c_void_p()
+        create = lib().tc_plan_create
         with torch.cuda.device(reps[0].device):  # the plan's streams live on the replicas' device
-            _check(lib().tc_plan_create(C.byref(d), C.byref(ptr)))
+            _check(create(C.byref(d), C.byref(ptr)))
         self._p = ptr
         self.handle = None
         _LIVE.add(self)

@@ -86,6 +86,7 @@ Layout compute_layout(uint32_t P, uint32_t G, uint64_t npieces, uint64_t nwriter
   L.round_blk[0] = take(L.round_bytes);
   L.round_blk[1] = take(L.round_bytes);
   L.status = take(256);
+  L.hostio = take(kHostioFlags + (uint64_t)G * 4);
   L.shares = take((nwriters + 1) * sizeof(ShareD));
   L.share_ctr = take(nwriters * 64);  // one counter per 64-byte line
   L.total = off;
@@ -349,11 +350,14 @@ __device__ void copy_2d(const EngineArgs& a, uint32_t p, const PieceD& pc) {
 }
 
 // The sum of global chunk g's mark stripes, per lane (each lane its own g).
+// One load in flight at a time: the publisher is not in a hurry, and every
+// register the engine kernel needs beyond the copy loop's is one less for a
+// producer sharing the SIMD.
 __device__ inline uint64_t lane_mark_count(const EngineArgs& a, uint32_t g) {
   const uint64_t* s = reinterpret_cast<const uint64_t*>(a.marks + (uint64_t)g * TC_MARK_STRIPES *
                                                                        TC_MARK_STRIPE_BYTES);
   uint64_t sum = 0;
-#pragma unroll
+#pragma unroll 1
   for (uint32_t k = 0; k < TC_MARK_STRIPES; ++k)
     sum += __hip_atomic_load(s + k * (TC_MARK_STRIPE_BYTES / 8), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
@@ -380,10 +384,9 @@ __device__ void publish_gates(const EngineArgs& a, uint64_t t0) {
     for (uint32_t base = 0; base < a.nchunks; base += 64) {
       const uint32_t g = base + lane;
       if (g < a.nchunks) {
-        const ChunkD cd = a.chunks[g];
-        uint64_t* ready = &gate_row(a, cd.rank, g)->ready;
+        uint64_t* ready = &gate_row(a, a.chunks[g].rank, g)->ready;
         if (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) < a.round) {
-          if (lane_mark_count(a, g) >= (uint64_t)a.round * cd.writers)
+          if (lane_mark_count(a, g) >= (uint64_t)a.round * a.chunks[g].writers)
             __hip_atomic_store(ready, (uint64_t)a.round, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
           else
             shut = 1;
@@ -393,8 +396,11 @@ __device__ void publish_gates(const EngineArgs& a, uint64_t t0) {
     if (__all(shut == 0)) return;
     if (wave_load_sys(a.force) != 0) return;
     if (must_stop(a, t0, ++spins)) return;
-    if (spins < 256) __builtin_amdgcn_s_sleep(2);
-    else __builtin_amdgcn_s_sleep(32);
+    // Gentle polling (about 1.7 us between passes after the first few):
+    // the publisher shares its CU with whatever runs beside the engine, and
+    // a producer made of one wave of tiles is as slow as its slowest CU.
+    if (spins < 8) __builtin_amdgcn_s_sleep(2);
+    else __builtin_amdgcn_s_sleep(64);
   }
 }
 
@@ -414,7 +420,12 @@ __global__ __launch_bounds__(kEngineThreads) void engine_kernel(EngineArgs a) {
     a.zero_round[i] = 0;
 
   const uint64_t t0 = now_ticks();
-  if (gw == 0) {  // global wave 0 publishes the gates' `ready` words and copies nothing
+  // The grid's last wave publishes the gates' `ready` words and copies
+  // nothing.  (Measured beside the GEMM producers: a wave of the first CTA
+  // that leaves the copy loop, even one that does nothing at all, costs
+  // the GEMMs running beside the engine about 25%; the last CTA's costs
+  // nothing measurable.)
+  if (gw == gridDim.x * (kEngineThreads / 64) - 1) {
     publish_gates(a, t0);
     return;
   }
@@ -535,6 +546,7 @@ __global__ __launch_bounds__(kCheckThreads) void check_kernel(CheckArgs a) {
 }  // namespace
 
 // ------------------------------------------------------------ host side
+
 
 int hip_fail(hipError_t e, const char* what) {
   return fail(TC_EHIP, std::string(what) + ": " + hipGetErrorString(e));
@@ -699,15 +711,45 @@ static int event_done_by(hipEvent_t ev, std::chrono::steady_clock::time_point de
 }
 
 // Spins until the check kernel has published sequence number `seq`, or the
-// deadline passes.  1 = done, 0 = deadline.
-static int check_done_by(const tc_plan* P, uint32_t seq,
-                         std::chrono::steady_clock::time_point deadline) {
+// deadline passes.  1 = done, 0 = deadline, negative = error.  A plan
+// without mapped host words (the no-allocation plans) waits for the check's
+// event instead and then copies its flags and status word back.
+static int check_done_by(tc_plan* P, uint32_t seq, std::chrono::steady_clock::time_point deadline) {
   int spins = 0;
   for (;;) {
-    if (__atomic_load_n(P->seq_host, __ATOMIC_ACQUIRE) == seq) return 1;
+    if (P->noalloc) {
+      const hipError_t e = hipEventQuery(P->ev_check_done);
+      if (e == hipSuccess) {
+        const uint8_t* io = P->ws + P->L.hostio;
+        TC_HIP(hipMemcpyAsync(&P->status_word, io + kHostioStatus, 4, hipMemcpyDeviceToHost,
+                              P->aux_stream));
+        if (P->G)
+          TC_HIP(hipMemcpyAsync(P->flags_buf.data(), io + kHostioFlags, (size_t)P->G * 4,
+                                hipMemcpyDeviceToHost, P->aux_stream));
+        TC_HIP(hipStreamSynchronize(P->aux_stream));
+        return 1;
+      }
+      if (e != hipErrorNotReady) return hip_fail(e, "wait: hipEventQuery (completion check)");
+    } else if (__atomic_load_n(P->seq_host, __ATOMIC_ACQUIRE) == seq) {
+      return 1;
+    }
     if (std::chrono::steady_clock::now() >= deadline) return 0;
     if (++spins > 20000) std::this_thread::sleep_for(std::chrono::microseconds(20));
   }
+}
+
+// Raises the abort word for the plan's newest engine launch: a store to
+// pinned host memory, or for a no-allocation plan a copy into its device
+// word on the side stream.
+static int set_abort(tc_plan* P) {
+  if (!P->noalloc) {
+    __atomic_store_n(P->abort_host, P->launch_id, __ATOMIC_SEQ_CST);
+    return TC_OK;
+  }
+  P->abort_value = P->launch_id;
+  TC_HIP(hipMemcpyAsync(P->abort_dev, &P->abort_value, 4, hipMemcpyHostToDevice, P->aux_stream));
+  TC_HIP(hipStreamSynchronize(P->aux_stream));
+  return TC_OK;
 }
 
 // Whether every gate of plan Q is open in its current round (or forced
@@ -801,14 +843,18 @@ static void destroy(tc_plan* P) {
     std::lock_guard<std::mutex> lock(R.mu);
     R.live.erase(std::remove(R.live.begin(), R.live.end(), P), R.live.end());
   }
-  if (P->aux_stream) (void)hipStreamDestroy(P->aux_stream);
   for (hipEvent_t e : {P->ev_prod_start, P->ev_prod_end, P->ev_engine_start, P->ev_engine_done,
                        P->ev_check_done})
     if (e) (void)hipEventDestroy(e);
-  if (P->abort_host) (void)hipHostFree((void*)P->abort_host);
-  if (P->flags_host) (void)hipHostFree(P->flags_host);
-  if (P->status_host) (void)hipHostFree(P->status_host);
-  if (P->seq_host) (void)hipHostFree((void*)P->seq_host);
+  if (P->noalloc) {
+    // The side stream and the workspace belong to the device, not the plan.
+  } else {
+    if (P->aux_stream) (void)hipStreamDestroy(P->aux_stream);
+    if (P->abort_host) (void)hipHostFree((void*)P->abort_host);
+    if (P->flags_host) (void)hipHostFree(P->flags_host);
+    if (P->status_host) (void)hipHostFree(P->status_host);
+    if (P->seq_host) (void)hipHostFree((void*)P->seq_host);
+  }
   delete P;
 }
 
@@ -838,15 +884,20 @@ int tc::check_device_range(const void* p, uint64_t bytes, int device, const char
 }
 }  // extern "C++"
 
-int tc_plan_create(const tc_plan_desc* d, tc_plan** out) {
+// Creates a plan over workspace `ws` (ws_bytes).  noalloc_aux != NULL: a
+// no-allocation plan, whose workspace is the device's `scratch` array, whose
+// side stream is the device's shared one, and whose host-visible words live
+// in its workspace instead of mapped host memory.
+static int create_plan(const tc_plan_desc* d, uint8_t* ws, uint64_t ws_bytes,
+                       hipStream_t noalloc_aux, int noalloc_device, tc_plan** out) {
   if (!out) return fail(TC_EINVAL, "out is NULL");
   *out = nullptr;
   if (int rc = tc_plan_validate(d)) return rc;
-  if (!d->replicas || !d->workspace) return fail(TC_EINVAL, "replicas or workspace is NULL");
+  if (!d->replicas || !ws) return fail(TC_EINVAL, "replicas or workspace is NULL");
   for (uint32_t p = 0; p < d->nranks; ++p)
     if (!d->replicas[p] || ((uintptr_t)d->replicas[p] & 255))
       return fail(TC_EINVAL, "replica pointers must be non-NULL and 256-byte aligned");
-  if ((uintptr_t)d->workspace & 255) return fail(TC_EINVAL, "workspace must be 256-byte aligned");
+  if ((uintptr_t)ws & 255) return fail(TC_EINVAL, "workspace must be 256-byte aligned");
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev == 0) return fail(TC_ENODEV, "no GPU visible");
   {
@@ -856,24 +907,33 @@ int tc_plan_create(const tc_plan_desc* d, tc_plan** out) {
       if (int rc = check_device_range(d->replicas[p], d->buffer_bytes, dev,
                                       ("replica " + std::to_string(p)).c_str()))
         return rc;
-    if (int rc = check_device_range(d->workspace, d->workspace_bytes, dev, "workspace")) return rc;
+    if (!noalloc_aux)
+      if (int rc = check_device_range(ws, ws_bytes, dev, "workspace")) return rc;
   }
 
   auto* P = new tc_plan();
   P->P = d->nranks;
   P->buffer_bytes = d->buffer_bytes;
   for (uint32_t p = 0; p < d->nranks; ++p) P->rep[p] = (uint8_t*)d->replicas[p];
-  P->ws = (uint8_t*)d->workspace;
-  P->ws_bytes = d->workspace_bytes;
+  P->ws = ws;
+  P->ws_bytes = ws_bytes;
   const uint64_t piece_bytes = d->piece_bytes ? d->piece_bytes : kDefaultPieceBytes;
   build_pieces(P->P, d->schedules, piece_bytes, P->pieces, P->chunks, P->piece_base, P->chunk_base);
   P->G = (uint32_t)P->chunks.size();
   for (const ChunkD& c : P->chunks) P->total_writers += c.writers;
   P->L = compute_layout(P->P, P->G, P->pieces.size(), P->total_writers);
-  if (P->L.total > d->workspace_bytes) {
+  if (P->L.total > ws_bytes) {
     const uint64_t need = P->L.total;
     delete P;
-    return fail(TC_ENOMEM, "workspace too small: need " + std::to_string(need) + " bytes");
+    return fail(TC_ENOMEM, std::string(noalloc_aux ? "the no-allocation workspace (" +
+                                                         std::to_string(ws_bytes) + " bytes)"
+                                                   : std::string("workspace")) +
+                               " is too small: the plan needs " + std::to_string(need) + " bytes");
+  }
+  if (noalloc_aux) {
+    P->noalloc = true;
+    P->device = noalloc_device;
+    P->aux_stream = noalloc_aux;
   }
   auto bail = [&](int rc) {
     destroy(P);
@@ -904,30 +964,45 @@ int tc_plan_create(const tc_plan_desc* d, tc_plan** out) {
   for (uint32_t m : mask) usable += __builtin_popcount(m);
   if (usable == 0) return bail(fail(TC_EINVAL, "cu_mask selects no CU"));
   if ((rc = engine_stream_for(P->device, mask, &P->engine_stream))) return bail(rc);
-  TC_HIP_C(hipStreamCreateWithFlags(&P->aux_stream, hipStreamNonBlocking));
+  if (!P->noalloc) TC_HIP_C(hipStreamCreateWithFlags(&P->aux_stream, hipStreamNonBlocking));
   TC_HIP_C(hipEventCreateWithFlags(&P->ev_prod_start, hipEventDisableTiming));
   TC_HIP_C(hipEventCreateWithFlags(&P->ev_prod_end, hipEventDisableTiming));
   TC_HIP_C(hipEventCreate(&P->ev_engine_start));
   TC_HIP_C(hipEventCreate(&P->ev_engine_done));
   TC_HIP_C(hipEventCreateWithFlags(&P->ev_check_done, hipEventDisableTiming));
-  void* hp = nullptr;
-  TC_HIP_C(hipHostMalloc(&hp, 64, hipHostMallocMapped | hipHostMallocCoherent));
-  P->abort_host = (volatile uint32_t*)hp;
-  P->abort_host[0] = 0;
-  TC_HIP_C(hipHostGetDevicePointer((void**)&P->abort_dev, hp, 0));
-  TC_HIP_C(hipHostMalloc((void**)&P->flags_host, (size_t)std::max<uint32_t>(P->G, 1) * 4,
-                         hipHostMallocMapped | hipHostMallocCoherent));
-  TC_HIP_C(hipHostGetDevicePointer((void**)&P->flags_dev, P->flags_host, 0));
-  TC_HIP_C(hipHostMalloc((void**)&P->status_host, 64, hipHostMallocMapped | hipHostMallocCoherent));
-  TC_HIP_C(hipHostGetDevicePointer((void**)&P->status_dev, P->status_host, 0));
-  TC_HIP_C(hipHostMalloc((void**)&P->seq_host, 64, hipHostMallocMapped | hipHostMallocCoherent));
-  *P->seq_host = 0;
-  TC_HIP_C(hipHostGetDevicePointer((void**)&P->seq_dev, (void*)P->seq_host, 0));
+  if (P->noalloc) {
+    // The engine's abort word and the check's outputs live in the
+    // workspace; the host copies them over the side stream.
+    uint8_t* io = P->ws + P->L.hostio;
+    P->abort_dev = reinterpret_cast<uint32_t*>(io + kHostioAbort);
+    P->status_dev = reinterpret_cast<uint32_t*>(io + kHostioStatus);
+    P->seq_dev = reinterpret_cast<uint32_t*>(io + kHostioSeq);
+    P->flags_dev = reinterpret_cast<uint32_t*>(io + kHostioFlags);
+    P->flags_buf.assign(std::max<uint32_t>(P->G, 1), 0u);
+    P->flags_host = P->flags_buf.data();
+    P->status_host = &P->status_word;
+  } else {
+    void* hp = nullptr;
+    TC_HIP_C(hipHostMalloc(&hp, 64, hipHostMallocMapped | hipHostMallocCoherent));
+    P->abort_host = (volatile uint32_t*)hp;
+    P->abort_host[0] = 0;
+    TC_HIP_C(hipHostGetDevicePointer((void**)&P->abort_dev, hp, 0));
+    TC_HIP_C(hipHostMalloc((void**)&P->flags_host, (size_t)std::max<uint32_t>(P->G, 1) * 4,
+                           hipHostMallocMapped | hipHostMallocCoherent));
+    TC_HIP_C(hipHostGetDevicePointer((void**)&P->flags_dev, P->flags_host, 0));
+    TC_HIP_C(hipHostMalloc((void**)&P->status_host, 64, hipHostMallocMapped | hipHostMallocCoherent));
+    TC_HIP_C(hipHostGetDevicePointer((void**)&P->status_dev, P->status_host, 0));
+    TC_HIP_C(hipHostMalloc((void**)&P->seq_host, 64, hipHostMallocMapped | hipHostMallocCoherent));
+    *P->seq_host = 0;
+    TC_HIP_C(hipHostGetDevicePointer((void**)&P->seq_dev, (void*)P->seq_host, 0));
+  }
 
-  // Zero the workspace (gates start at zero, [TP] Gates and rounds), then
-  // upload the descriptors once.
-  if ((rc = zero_device(P->ws, P->L.total, P->engine_stream))) return bail(rc);
-  TC_HIP_C(hipStreamSynchronize(P->engine_stream));
+  // Zero the workspace (gates start at zero, [TP] Gates and rounds; a
+  // no-allocation workspace also still holds the previous plan's state),
+  // then upload the descriptors once.  Both go over the plan's side stream,
+  // which is non-blocking: the shared engine stream, or the legacy stream
+  // that waits for it, may hold another plan's engine waiting on its gates.
+  if ((rc = zero_device(P->ws, P->L.total, P->aux_stream))) return bail(rc);
   std::vector<uint32_t> writers(P->G);
   std::vector<uint64_t> wprefix(P->G + 1, 0);
   for (uint32_t g = 0; g < P->G; ++g) {
@@ -936,14 +1011,17 @@ int tc_plan_create(const tc_plan_desc* d, tc_plan** out) {
   }
   P->total_writers = wprefix[P->G];
   if (!P->pieces.empty())
-    TC_HIP_C(hipMemcpy(P->ws + P->L.pieces, P->pieces.data(), P->pieces.size() * sizeof(PieceD),
-                       hipMemcpyHostToDevice));
+    TC_HIP_C(hipMemcpyAsync(P->ws + P->L.pieces, P->pieces.data(), P->pieces.size() * sizeof(PieceD),
+                            hipMemcpyHostToDevice, P->aux_stream));
   if (P->G) {
-    TC_HIP_C(hipMemcpy(P->ws + P->L.chunks, P->chunks.data(), P->G * sizeof(ChunkD),
-                       hipMemcpyHostToDevice));
-    TC_HIP_C(hipMemcpy(P->ws + P->L.writers, writers.data(), P->G * 4, hipMemcpyHostToDevice));
+    TC_HIP_C(hipMemcpyAsync(P->ws + P->L.chunks, P->chunks.data(), P->G * sizeof(ChunkD),
+                            hipMemcpyHostToDevice, P->aux_stream));
+    TC_HIP_C(hipMemcpyAsync(P->ws + P->L.writers, writers.data(), P->G * 4, hipMemcpyHostToDevice,
+                            P->aux_stream));
   }
-  TC_HIP_C(hipMemcpy(P->ws + P->L.wprefix, wprefix.data(), wprefix.size() * 8, hipMemcpyHostToDevice));
+  TC_HIP_C(hipMemcpyAsync(P->ws + P->L.wprefix, wprefix.data(), wprefix.size() * 8,
+                          hipMemcpyHostToDevice, P->aux_stream));
+  TC_HIP_C(hipStreamSynchronize(P->aux_stream));  // the host arrays above are about to go
 
   // One-shot fill table, when every chunk is one byte range: each writer's
   // share cut into kOneShotBlock blocks, every rank's chunk 0 first, then
@@ -982,7 +1060,9 @@ int tc_plan_create(const tc_plan_desc* d, tc_plan** out) {
     ShareD end{};
     end.first_block = blocks;
     sh.push_back(end);
-    TC_HIP_C(hipMemcpy(P->ws + P->L.shares, sh.data(), sh.size() * sizeof(ShareD), hipMemcpyHostToDevice));
+    TC_HIP_C(hipMemcpyAsync(P->ws + P->L.shares, sh.data(), sh.size() * sizeof(ShareD),
+                            hipMemcpyHostToDevice, P->aux_stream));
+    TC_HIP_C(hipStreamSynchronize(P->aux_stream));
     P->oneshot_blocks = blocks;
   }
 
@@ -1023,6 +1103,14 @@ int tc_plan_create(const tc_plan_desc* d, tc_plan** out) {
   }
   *out = P;
   return TC_OK;
+}
+
+int tc_plan_create(const tc_plan_desc* d, tc_plan** out) {
+  if (!d) {
+    if (out) *out = nullptr;
+    return fail(TC_EINVAL, "desc is NULL");
+  }
+  return create_plan(d, (uint8_t*)d->workspace, d->workspace_bytes, nullptr, 0, out);
 }
 
 int tc_plan_start(tc_plan* P, void* stream, tc_handle* out) {
@@ -1082,14 +1170,18 @@ int tc_plan_wait(tc_plan* P, uint64_t timeout_us) {
   }
   if (int rc = queue_check(P)) return rc;
   const uint32_t seq = P->check_seq;
-  const bool timed_out = check_done_by(P, seq, deadline) == 0;
+  const int first_check = check_done_by(P, seq, deadline);
+  if (first_check < 0) return first_check;
+  const bool timed_out = first_check == 0;
   if (timed_out) {
     // Stop this launch of the engine if it still runs (every poll loop
     // watches the abort word), then let the queued check finish.
     if (hipEventQuery(P->ev_engine_done) != hipSuccess)
-      __atomic_store_n(P->abort_host, P->launch_id, __ATOMIC_SEQ_CST);
+      if (int rc = set_abort(P)) return rc;
     const auto drain = std::chrono::steady_clock::now() + std::chrono::seconds(10);
-    if (check_done_by(P, seq, drain) == 0) {
+    const int drained = check_done_by(P, seq, drain);
+    if (drained < 0) return drained;
+    if (drained == 0) {
       P->need_relaunch = hipEventQuery(P->ev_engine_done) == hipSuccess;
       return fail(TC_ETIMEOUT, "wait: the copy engine or the producer did not finish within 10 s "
                                "of the deadline");
@@ -1204,7 +1296,7 @@ int tc_plan_close(tc_plan* P, int* closing) {
     }
     int done = event_done_by(P->ev_engine_done, deadline(10), &err);
     if (done != 1) {  // the forced engine did not finish: stop it
-      __atomic_store_n(P->abort_host, P->launch_id, __ATOMIC_SEQ_CST);
+      if (int rc = set_abort(P)) return rc;
       done = event_done_by(P->ev_engine_done, deadline(10), &err);
     }
     if (done != 1 || (P->check_seq && event_done_by(P->ev_check_done, deadline(10), &err) != 1)) {

@@ -16,6 +16,13 @@ constexpr uint32_t kStatsWords = 2;     // u64 words of per-launch timestamps
 
 constexpr uint64_t kForceOffset = 128;  // byte offset of the force word in the status block
 
+// The host-visible words of a no-allocation plan, in its workspace's hostio
+// segment (other plans keep them in mapped host memory): byte offsets.
+constexpr uint64_t kHostioAbort = 0;    // the engine's abort word
+constexpr uint64_t kHostioStatus = 64;  // the engine status handed over by the check
+constexpr uint64_t kHostioSeq = 128;    // the check's sequence word
+constexpr uint64_t kHostioFlags = 256;  // the check's per-chunk flags, G words
+
 constexpr uint32_t kStatusAborted = 1;  // engine stopped by the host's abort word
 constexpr uint32_t kStatusExpired = 2;  // engine stopped by its wall-clock backstop
 
@@ -32,6 +39,7 @@ struct Layout {
   uint64_t launch[2], launch_bytes;     // tickets | stats | stop | done, per launch parity
   uint64_t round_blk[2], round_bytes;   // sig | cursors, per round parity
   uint64_t status;
+  uint64_t hostio;                      // host-visible words of a no-allocation plan
   uint64_t shares, share_ctr;           // one-shot fill: share table and per-share counters
   uint64_t total;
 };
@@ -70,6 +78,10 @@ struct tc_plan {
   volatile uint32_t* seq_host = nullptr;    // pinned, mapped: the last check's sequence number
   uint32_t* seq_dev = nullptr;
   uint32_t check_seq = 0;
+  bool noalloc = false;                     // workspace = the device's static array
+  std::vector<uint32_t> flags_buf;          // no-allocation plan: the check's flags, copied back
+  uint32_t status_word = 0;                 // no-allocation plan: the status word, copied back
+  uint32_t abort_value = 0;                 // no-allocation plan: source of the abort copy
 
   uint32_t engine_ctas = 0;
   uint64_t backstop_ticks = 0;
