@@ -23,7 +23,9 @@
  *     owns every buffer it passes in.
  *   - The library allocates no device memory of its own: the caller passes a
  *     workspace (sized by tc_plan_workspace_bytes).  A plan allocates only
- *     small pinned host words, its streams and its events.
+ *     small pinned host words, its streams and its events.  The one
+ *     exception is tc_plan_create_noalloc, whose workspace is a static
+ *     device array of the library (for callers that cannot allocate).
  */
 #ifndef TC_H
 #define TC_H
@@ -248,6 +250,27 @@ int tc_plan_validate(const tc_plan_desc* desc);
  * another device gives TC_EINVAL, a size past the allocation's end TC_EBOUNDS.
  * Errors: TC_EINVAL, TC_EBOUNDS, TC_EOVERLAP, TC_ENOMEM, TC_EHIP, TC_ENODEV. */
 int tc_plan_create(const tc_plan_desc* desc, tc_plan** out);
+
+/* For callers that cannot allocate memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): tc_plan_create
+ * without a caller-supplied workspace and without any allocation of device
+ * or pinned host memory (no hipMalloc, hipHostMalloc or hipFree; the plan's
+ * own bookkeeping lives on the C++ heap, and it creates its HIP events).
+ * The workspace is a static device array of the library,
+ * TC_NOALLOC_WORKSPACE_BYTES per device, that each device holds until the
+ * process ends; the engine's abort word and the completion check's results
+ * live in it too, and the host reads them back with copies.  desc is as for
+ * tc_plan_create, with workspace = NULL and workspace_bytes = 0.  The array
+ * keeps the previous plan's contents; the plan zeroes what it uses.  All
+ * no-allocation plans of a device share the one array, so only one may be
+ * open per device at a time: a second is refused (TC_ESTATE) rather than
+ * left to race on it, and kernels still using a closed plan's handle race
+ * with the next plan.  The plan is then used and closed like any other.
+ * TC_ENOMEM when the plan's workspace (tc_plan_workspace_bytes) exceeds
+ * TC_NOALLOC_WORKSPACE_BYTES; TC_EINVAL for a non-NULL workspace; otherwise
+ * the errors of tc_plan_create. */
+#define TC_NOALLOC_WORKSPACE_BYTES (32ull << 20)
+int tc_plan_create_noalloc(const tc_plan_desc* desc, tc_plan** out);
 
 /* Starts the round ([TP] Model: start()).  READY -> STARTED.  The copy
  * engine is launched on the plan's stream behind all work already queued on

@@ -265,11 +265,14 @@ class TriggeredPlan:
     ``replicas``: a [P, B] uint8 CUDA tensor or a list of P CUDA tensors of
     equal byte size (256-byte aligned).  ``schedules``: P schedules (None =
     that rank sends nothing).  The workspace is a torch allocation unless
-    given.  Use as a context manager; leaving the block closes the plan.
+    given; with ``noalloc=True`` the plan is made by tc_plan_create_noalloc
+    and uses the library's static per-device workspace instead (one such
+    plan per device at a time).  Use as a context manager; leaving the block
+    closes the plan.
     """
 
     def __init__(self, replicas, schedules, *, own_rows_bytes=None, cu_mask=None,
-                 engine_ctas=0, piece_bytes=0, backstop_s=30.0, workspace=None):
+                 engine_ctas=0, piece_bytes=0, backstop_s=30.0, workspace=None, noalloc=False):
         import torch
         if isinstance(replicas, torch.Tensor) and replicas.dim() == 2:
             reps = [replicas[p] for p in range(replicas.shape[0])]
@@ -288,7 +291,9 @@ class TriggeredPlan:
         self._keep = (reps, list(schedules))
         sched_ptrs = (C.c_void_p * P)(*[s.ptr.value if s is not None else None for s in schedules])
         self._sched_ptrs = sched_ptrs
-        if workspace is None:
+        if noalloc and workspace is not None:
+            raise InvalidArgument("a no-allocation plan takes no workspace")
+        if workspace is None and not noalloc:
             ws_need = C.c_uint64()
             _check(lib().tc_plan_workspace_bytes(P, sched_ptrs, piece_bytes, C.byref(ws_need)))
             workspace = torch.empty(ws_need.value, dtype=torch.uint8, device=reps[0].device)
@@ -314,7 +319,7 @@ class TriggeredPlan:
         d.engine_backstop_us = int(backstop_s * 1e6)
         self._desc = d
         ptr = C.c_void_p()
-        create = lib().tc_plan_create
+        create = lib().tc_plan_create_noalloc if noalloc else lib().tc_plan_create
         with torch.cuda.device(reps[0].device):  # the plan's streams live on the replicas' device
             _check(create(C.byref(d), C.byref(ptr)))
         self._p = ptr

@@ -7,6 +7,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtriggered_copy.so")
 
 TC_MAX_RANKS = 16
+NOALLOC_WORKSPACE_BYTES = 32 << 20
 GATE_ROW_BYTES = 64
 
 OK, EINVAL, EBOUNDS, EOVERLAP, ENOMEM, EHIP, ESTATE, ETIMEOUT, EEXTRA, EROUNDS, ENODEV, ECORRUPT = \
@@ -70,6 +71,7 @@ _SIGS = {
     "tc_plan_workspace_bytes": [u32, C.POINTER(vp), u64, C.POINTER(u64)],
     "tc_plan_validate": [C.POINTER(PlanDesc)],
     "tc_plan_create": [C.POINTER(PlanDesc), C.POINTER(vp)],
+    "tc_plan_create_noalloc": [C.POINTER(PlanDesc), C.POINTER(vp)],
     "tc_plan_start": [vp, vp, C.POINTER(Handle)],
     "tc_plan_wait": [vp, u64],
     "tc_plan_handle": [vp, C.POINTER(Handle)],

@@ -547,6 +547,11 @@ __global__ __launch_bounds__(kCheckThreads) void check_kernel(CheckArgs a) {
 
 // ------------------------------------------------------------ host side
 
+// The workspace of no-allocation plans (tc_plan_create_noalloc): one array
+// per device, for the life of the process.  In host code the name stands in
+// for the symbol only; its address on a device comes from
+// hipGetSymbolAddress, once per device, and kernels get that address.
+static __device__ __align__(256) uint8_t scratch[TC_NOALLOC_WORKSPACE_BYTES];
 
 int hip_fail(hipError_t e, const char* what) {
   return fail(TC_EHIP, std::string(what) + ": " + hipGetErrorString(e));
@@ -566,11 +571,18 @@ int hip_fail(hipError_t e, const char* what) {
 // another plan's waiting engine, and tc_release() can destroy the streams
 // once no plan is left.  It is never destroyed itself, so nothing of it runs
 // in the process's exit-time destructors.
+struct NoallocDevice {
+  uint8_t* scratch = nullptr;  // this device's copy of `scratch`, from hipGetSymbolAddress
+  hipStream_t aux = nullptr;   // side stream shared by the device's no-allocation plans
+  bool in_use = false;         // a no-allocation plan is open on the device
+};
+
 struct Registry {
   std::mutex mu;
   std::map<std::pair<int, std::vector<uint32_t>>, hipStream_t> streams;
   std::vector<tc_plan*> live;
   uint64_t submits = 0;  // engine launches so far, in submission order
+  std::map<int, NoallocDevice> noalloc;
 };
 
 static Registry& registry() {
@@ -848,6 +860,9 @@ static void destroy(tc_plan* P) {
     if (e) (void)hipEventDestroy(e);
   if (P->noalloc) {
     // The side stream and the workspace belong to the device, not the plan.
+    Registry& R = registry();
+    std::lock_guard<std::mutex> lock(R.mu);
+    R.noalloc[P->device].in_use = false;
   } else {
     if (P->aux_stream) (void)hipStreamDestroy(P->aux_stream);
     if (P->abort_host) (void)hipHostFree((void*)P->abort_host);
@@ -1113,6 +1128,55 @@ int tc_plan_create(const tc_plan_desc* d, tc_plan** out) {
   return create_plan(d, (uint8_t*)d->workspace, d->workspace_bytes, nullptr, 0, out);
 }
 
+int tc_plan_create_noalloc(const tc_plan_desc* d, tc_plan** out) {
+  if (!out) return fail(TC_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (int rc = tc_plan_validate(d)) return rc;
+  if (d->workspace || d->workspace_bytes)
+    return fail(TC_EINVAL, "create_noalloc: the plan uses the library's own workspace; pass "
+                           "workspace = NULL and workspace_bytes = 0");
+  uint64_t need = 0;
+  if (int rc = tc_plan_workspace_bytes(d->nranks, d->schedules, d->piece_bytes, &need)) return rc;
+  if (need > TC_NOALLOC_WORKSPACE_BYTES)
+    return fail(TC_ENOMEM, "create_noalloc: the plan needs a " + std::to_string(need) +
+                               "-byte workspace; a no-allocation plan has at most " +
+                               std::to_string(TC_NOALLOC_WORKSPACE_BYTES) +
+                               " (use tc_plan_create with a workspace of its own)");
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(TC_EHIP, "create_noalloc: hipGetDevice failed");
+  Registry& R = registry();
+  uint8_t* ws = nullptr;
+  hipStream_t aux = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(R.mu);
+    NoallocDevice& nd = R.noalloc[dev];
+    if (nd.in_use)
+      return fail(TC_ESTATE, "create_noalloc: a no-allocation plan is already open on device " +
+                                 std::to_string(dev) + " (they share one workspace)");
+    if (!nd.scratch) {
+      // Once per device, with the device current: the array's address on
+      // this device (the name itself is only a host-side stand-in).
+      void* ptr = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e, "create_noalloc: hipGetSymbolAddress(scratch)");
+      nd.scratch = (uint8_t*)ptr;
+    }
+    if (!nd.aux) {
+      const hipError_t e = hipStreamCreateWithFlags(&nd.aux, hipStreamNonBlocking);
+      if (e != hipSuccess) return hip_fail(e, "create_noalloc: hipStreamCreateWithFlags");
+    }
+    nd.in_use = true;
+    ws = nd.scratch;
+    aux = nd.aux;
+  }
+  const int rc = create_plan(d, ws, TC_NOALLOC_WORKSPACE_BYTES, aux, dev, out);
+  if (rc != TC_OK) {
+    std::lock_guard<std::mutex> lock(R.mu);
+    R.noalloc[dev].in_use = false;
+  }
+  return rc;
+}
+
 int tc_plan_start(tc_plan* P, void* stream, tc_handle* out) {
   if (!P || !out) return fail(TC_EINVAL, "start: NULL argument");
   if (P->state != TC_STATE_READY) return fail(TC_ESTATE, "start() needs a READY plan");
@@ -1319,6 +1383,12 @@ int tc_release(void) {
     if (e != hipSuccess && rc == TC_OK) rc = hip_fail(e, "release: hipStreamDestroy (engine stream)");
   }
   R.streams.clear();
+  for (auto& kv : R.noalloc) {
+    if (!kv.second.aux) continue;
+    const hipError_t e = hipStreamDestroy(kv.second.aux);
+    if (e != hipSuccess && rc == TC_OK) rc = hip_fail(e, "release: hipStreamDestroy (side stream)");
+    kv.second.aux = nullptr;
+  }
   return rc;
 }
 
