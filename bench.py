@@ -481,9 +481,111 @@ def cpu_baseline(workloads, seed, budget_s=12.0):
             break
     dt = (time.perf_counter() - t0) / n
     return {"value": P * (P - 1) * nb / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "s_per_round": dt,
             "sample": f"P={P}, {rows}x{cols} u32 per rank ({nb / 2**20:.0f} MiB, 1/96 of the rows), "
                       f"chunks({w['n']}), {w['writers']} writers, {n} full oracle rounds "
                       f"(produce + marks + in-order copies + wait) in {dt * n:.1f} s on one core"}
+
+
+def oracle_per_config(workloads, seed, budget_s=2.0):
+    """The oracle, as it stands, timed per workload on one host core: seconds
+    per round (at least one round, then as many as fit in budget_s).  The
+    small workloads run at their full sizes; the 1.5 GiB one is the sample
+    that cpu_baseline times (its full-size figure is that scaled by the row
+    ratio).  The GEMM workload's round is the plan simulation fed each
+    rank's block, with the fp32 reference GEMMs timed beside it."""
+    import numpy as np
+    import torch
+    from oracle import barrier as obarrier
+    from oracle import gemm as ogemm
+    from oracle import plan as oplan
+    from oracle import schedule as osched
+    from oracle import values as ovalues
+    from synth import gemm_operands, shuffled_order
+    e_of = {"u32": 4, "bf16": 2, "u8": 1}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            fn()
+            n += 1
+            if time.perf_counter() - t0 > budget_s:
+                return (time.perf_counter() - t0) / n, n
+
+    def sim_of(w):
+        e = e_of[w["elem"]]
+        P, rows, cols = w["P"], w["rows"], w["cols"]
+        nb = rows * cols * e
+        ov = [osched.View(p * nb, rows, cols, cols, e) for p in range(P)]
+        if w["builder"] == "whole":
+            sch = [osched.whole(v, w["writers"]) for v in ov]
+        elif w["builder"] == "chunks":
+            sch = [osched.chunks(v, w["n"], w["writers"]) for v in ov]
+        else:
+            tm, tn = -(-rows // w["bm"]), -(-cols // w["bn"])
+            order = ([osched.tile_of(i, tm, tn, w["group_m"]) for i in range(tm * tn)]
+                     if w.get("group_m") else None)
+            sch = [osched.tile_chunks(v, w["bm"], w["bn"], w["tiles_per_chunk"], order) for v in ov]
+        reps = [np.full(P * nb, 0xA5, dtype=np.uint8) for _ in range(P)]
+        return oplan.PlanSim(reps, sch), nb
+
+    def fill_round(name, order_of=None):
+        w = workloads.FULL[name]
+        sim, nb = sim_of(w)
+        P, e = w["P"], e_of[w["elem"]]
+
+        def produce(p, r):
+            sim.rep[p][p * nb:(p + 1) * nb] = ovalues.block_bytes(w["elem"], seed, p, r, nb // e)
+
+        def one():
+            marks = order_of(sim) if order_of else None
+            oplan.run_round(sim, produce, mark_order=marks)
+            sim.next_round()
+        dt, n = timed(one)
+        return {"s_per_round": dt, "rounds": n, "delivered_bytes": P * (P - 1) * nb}
+
+    out = {}
+    threads = torch.get_num_threads()
+    torch.set_num_threads(1)
+    try:
+        out["bf16_chunks_p2"] = fill_round("bf16_chunks_p2")
+        out["u32_whole_p8"] = fill_round("u32_whole_p8")
+
+        def shuffled(sim):
+            n = max(sim.n)
+            return [(p, int(c)) for p in range(sim.P) for c in shuffled_order(seed, p, sim.round, n)
+                    for _ in range(sim.writers(p, int(c)))]
+        out["u32_tiles_shuffled_p8"] = fill_round("u32_tiles_shuffled_p8", shuffled)
+
+        w = workloads.FULL["gemm_tiles_p4"]
+        P, M, N, K = w["P"], w["rows"], w["cols"], w["K"]
+        sim, nb = sim_of(w)
+        ops = [gemm_operands(seed, p, 1, M, N, K) for p in range(P)]
+        t0 = time.perf_counter()
+        refs = [ogemm.gemm_ref(a, bt) for a, bt in ops]
+        ref_s = time.perf_counter() - t0
+        blocks = [(r.view(np.uint32) >> np.uint32(16)).astype(np.uint16).view(np.uint8).reshape(-1)
+                  for r in refs]
+
+        def produce(p, r):
+            sim.rep[p][p * nb:(p + 1) * nb] = blocks[p]
+
+        def one():
+            oplan.run_round(sim, produce)
+            sim.next_round()
+        dt, n = timed(one)
+        out["gemm_tiles_p4"] = {"s_per_round": dt, "rounds": n, "delivered_bytes": P * (P - 1) * nb,
+                                "fp32_reference_gemms_s": ref_s}
+
+        wb = workloads.FULL["barrier_p8"]
+        t0 = time.perf_counter()
+        obarrier.run(wb["P"], wb["gens"])
+        obarrier.reveal(wb["P"], 1, wb["gens"])
+        out["barrier_p8"] = {"s_per_1000_generations": time.perf_counter() - t0}
+    finally:
+        torch.set_num_threads(threads)
+    return out
 
 
 def cpu_copy_baseline(workloads, sample_bytes=256 << 20, reps=5):
@@ -629,6 +731,13 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline: the oracle on a bounded sample")
         cpu = cpu_baseline(workloads, BASE_SEED)
+        log("cpu baseline: the oracle per workload, one core")
+        per = oracle_per_config(workloads, BASE_SEED)
+        per["u32_chunks_1p5g_p4"] = {"s_per_round_sample": cpu["s_per_round"],
+                                     "s_per_round_full_estimate": cpu["s_per_round"] * 96,
+                                     "sample": "1/96 of the rows"}
+        cpu["per_config"] = per
+        cpu.pop("s_per_round")
         log("cpu copy baseline: numpy.copyto of one GPU's share, sampled")
         extras["cpu_copy_baseline"] = cpu_copy_baseline(workloads)
     line = {
