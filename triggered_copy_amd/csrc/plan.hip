@@ -16,9 +16,10 @@
 //    CUs at once and the addresses in flight stay within a narrow window.
 //  * A wave reading a chunk for the first time polls its gate: the chunk's
 //    mark count (the sum of its stripes) >= round * writers, or the plan's
-//    force word set by a close() in mid-round.  Data is read with
-//    device-scope loads, which return the coherent copy, so no cache
-//    invalidate is needed after the gate.
+//    force word set by a close() in mid-round.  Data is read with loads of
+//    device-scope coherence (sc1, the policy of a device-scope atomic load),
+//    each of which reads the coherent copy, so no cache invalidate is needed
+//    after the gate (it would be for ordinary loads).
 //  * A piece is read once and written to all P-1 other replicas (fan-out): the
 //    P per-peer queues of one source see the same gates, so they advance
 //    together and delivering to all of them at once changes no outcome.
@@ -108,11 +109,11 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kEngineThreads = 256;     // 4 independent waves per CTA
 constexpr int kUnroll = 2;              // 16-byte vectors in flight per lane per step
 constexpr int kBufWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
-// Cache policy of the engine's buffer accesses: loads at device scope (sc1)
-// read the coherent copy, so no L2 invalidate is needed after a gate opens;
-// stores at system scope (sc0 sc1) are written through, so their completion
-// (vmcnt) already means "visible", and no L2 write-back is needed before an
-// arrival is signalled.
+// Cache policy of the engine's buffer accesses: loads at device scope (sc1,
+// as a device-scope atomic load) read the coherent copy, so no L2
+// invalidate is needed after a gate opens; stores at system scope (sc0 sc1)
+// are written through, so their completion (vmcnt) already means
+// "visible", and no L2 write-back is needed before an arrival is signalled.
 constexpr int kLoadPolicy = 16;
 constexpr int kStorePolicy = 17;
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;  // offset past every buffer: access dropped
@@ -205,6 +206,18 @@ __device__ inline bool must_stop(const EngineArgs& a, uint64_t t0, uint32_t spin
 // briskly: they are on the round's critical path.
 constexpr int kPollNormal = 0, kPollReserve = 1, kPollBrisk = 2;
 
+// The pause after the spins-th fruitless poll in a row.
+__device__ inline void backoff(int mode, uint32_t spins) {
+  if (spins < 8 || mode == kPollBrisk) {
+    __builtin_amdgcn_s_sleep(1);
+  } else if (mode == kPollNormal) {
+    if (spins < 64) __builtin_amdgcn_s_sleep(16);
+    else __builtin_amdgcn_s_sleep(64);
+  } else {
+    for (int k = 0; k < 6; ++k) __builtin_amdgcn_s_sleep(127);
+  }
+}
+
 // Uniform spin until ready() holds.
 template <typename Ready>
 __device__ inline bool poll_until(const EngineArgs& a, uint64_t t0, int mode, Ready ready) {
@@ -215,14 +228,7 @@ __device__ inline bool poll_until(const EngineArgs& a, uint64_t t0, int mode, Re
       return true;
     }
     if (must_stop(a, t0, ++spins)) return false;
-    if (spins < 8 || mode == kPollBrisk) {
-      __builtin_amdgcn_s_sleep(1);
-    } else if (mode == kPollNormal) {
-      if (spins < 64) __builtin_amdgcn_s_sleep(16);
-      else __builtin_amdgcn_s_sleep(64);
-    } else {
-      for (int k = 0; k < 6; ++k) __builtin_amdgcn_s_sleep(127);
-    }
+    backoff(mode, spins);
   }
 }
 
@@ -350,14 +356,11 @@ __device__ void copy_2d(const EngineArgs& a, uint32_t p, const PieceD& pc) {
 }
 
 // The sum of global chunk g's mark stripes, per lane (each lane its own g).
-// One load in flight at a time: the publisher is not in a hurry, and every
-// register the engine kernel needs beyond the copy loop's is one less for a
-// producer sharing the SIMD.
 __device__ inline uint64_t lane_mark_count(const EngineArgs& a, uint32_t g) {
   const uint64_t* s = reinterpret_cast<const uint64_t*>(a.marks + (uint64_t)g * TC_MARK_STRIPES *
                                                                        TC_MARK_STRIPE_BYTES);
   uint64_t sum = 0;
-#pragma unroll 1
+#pragma unroll
   for (uint32_t k = 0; k < TC_MARK_STRIPES; ++k)
     sum += __hip_atomic_load(s + k * (TC_MARK_STRIPE_BYTES / 8), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
@@ -396,11 +399,9 @@ __device__ void publish_gates(const EngineArgs& a, uint64_t t0) {
     if (__all(shut == 0)) return;
     if (wave_load_sys(a.force) != 0) return;
     if (must_stop(a, t0, ++spins)) return;
-    // Gentle polling (about 1.7 us between passes after the first few):
-    // the publisher shares its CU with whatever runs beside the engine, and
-    // a producer made of one wave of tiles is as slow as its slowest CU.
-    if (spins < 8) __builtin_amdgcn_s_sleep(2);
-    else __builtin_amdgcn_s_sleep(64);
+    // Brisk polling: the engine cannot end before the publisher, so its pass
+    // interval is on the round's critical path.
+    __builtin_amdgcn_s_sleep(2);
   }
 }
 
@@ -655,12 +656,14 @@ static int launch_engine(tc_plan* P) {
     TC_HIP(hipEventElapsedTime(&P->last_engine_ms, P->ev_engine_start, P->ev_engine_done));
     P->engine_ms_pending = false;
   }
-  TC_HIP(hipEventRecord(P->ev_engine_start, P->engine_stream));
   {
     Registry& R = registry();
     std::lock_guard<std::mutex> lock(R.mu);
-    hipLaunchKernelGGL(engine_kernel, dim3(P->engine_ctas), dim3(kEngineThreads), 0, P->engine_stream,
-                       a);
+    // (Events attached to the dispatch itself, hipExtLaunchKernelGGL,
+    // measured slower: 2-rank rounds 76 against 62-66 us, and the GEMMs
+    // beside the engine 7% against 4% slower.)
+    TC_HIP(hipEventRecord(P->ev_engine_start, P->engine_stream));
+    hipLaunchKernelGGL(engine_kernel, dim3(P->engine_ctas), dim3(kEngineThreads), 0, P->engine_stream, a);
     P->last_submit = ++R.submits;
   }
   TC_HIP(hipGetLastError());
