@@ -145,6 +145,17 @@ struct EngineArgs {
   uint32_t launch_id;
   uint32_t nchunks;       // G
   uint64_t backstop_ticks;
+  // The completion check, run by the publisher once every chunk is
+  // signalled and the host has asked for it (chk_seq == 0: not this launch).
+  uint32_t chk_seq;             // sequence number of the check this launch may run
+  uint32_t pad2;
+  const uint32_t* chk_req;      // mapped host word: the host writes chk_seq to ask
+  uint32_t* chk_exit;           // mapped host word: launch id, when it left without checking
+  uint32_t* chk_flags;          // mapped host memory: one flag word per chunk
+  uint32_t* chk_status;         // mapped host word: the engine status handed over
+  uint32_t* chk_seq_host;       // mapped host word: chk_seq once the flags are written
+  uint32_t chunk_base[TC_MAX_RANKS + 1];
+  uint32_t pad3;
 };
 
 __device__ inline uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
@@ -355,6 +366,70 @@ __device__ void copy_2d(const EngineArgs& a, uint32_t p, const PieceD& pc) {
   }
 }
 
+// What the completion check reads: the workspace's chunk descriptors, gate
+// tables and mark stripes, against round `round`.
+struct CheckView {
+  const ChunkD* chunks;
+  const uint8_t* gates;
+  uint64_t gate_stride;
+  const uint8_t* marks;
+  uint32_t nranks, round;
+};
+
+__device__ inline uint64_t ld(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Flags of global chunk g: its counters against what a complete round r
+// leaves ([TP] Gates and rounds: this rank's chunk marked by all its writers
+// and arrived at every peer).  Per lane.
+__device__ uint32_t check_chunk(const CheckView& a, uint32_t g) {
+  const ChunkD cd = a.chunks[g];
+  const uint64_t want = (uint64_t)a.round * cd.writers;
+  uint64_t marks = 0;
+  for (uint32_t k = 0; k < TC_MARK_STRIPES; ++k)
+    marks += ld(reinterpret_cast<const uint64_t*>(
+        a.marks + ((uint64_t)g * TC_MARK_STRIPES + k) * TC_MARK_STRIPE_BYTES));
+  uint32_t f = 0;
+  if (marks > want) f |= kFlagExtra;
+  if (marks < want) f |= kFlagShortMarks;
+  for (uint32_t q = 0; q < a.nranks; ++q) {
+    const tc_gate_row* r = reinterpret_cast<const tc_gate_row*>(
+        a.gates + (uint64_t)q * a.gate_stride + (uint64_t)g * TC_GATE_ROW_BYTES);
+    for (int k = 0; k < 5; ++k)
+      if (ld(&r->rsvd[k]) != 0) f |= kFlagCorrupt;
+    if (ld(&r->writers) != 0) f |= kFlagCorrupt;
+    const uint64_t arr = ld(&r->arrival);
+    const uint64_t rdy = ld(&r->ready);
+    if (q == cd.rank) {
+      // The sender's row: no arrival; `ready` is this round once the gate
+      // has opened (it is stored before the chunk is signalled anywhere).
+      if (arr != 0 || rdy > a.round) f |= kFlagCorrupt;
+      if (rdy < a.round) f |= kFlagNotArrived;
+      continue;
+    }
+    if (rdy != 0) f |= kFlagCorrupt;
+    if (arr < a.round) f |= kFlagNotArrived;
+    if (arr > a.round) f |= kFlagCorrupt;
+  }
+  return f;
+}
+
+struct CheckArgs {
+  CheckView v;
+  uint32_t* flags;        // mapped pinned host memory, one word per chunk
+  uint32_t* status;       // device engine status word: read, reported, cleared
+  uint32_t* status_host;  // mapped pinned host memory
+  uint32_t* seq_host;     // mapped pinned host memory: `seq` once every flag is written
+  uint32_t G, seq;
+};
+
+constexpr int kCheckThreads = 1024;
+// Plans of up to this many chunks have their completion check run by the
+// engine's publisher (one wave, 64 chunks at a time); larger ones by the
+// check kernel.
+constexpr uint32_t kEngineCheckMaxChunks = 256;
+
 // The sum of global chunk g's mark stripes, per lane (each lane its own g).
 __device__ inline uint64_t lane_mark_count(const EngineArgs& a, uint32_t g) {
   const uint64_t* s = reinterpret_cast<const uint64_t*>(a.marks + (uint64_t)g * TC_MARK_STRIPES *
@@ -380,7 +455,7 @@ __device__ inline uint64_t lane_mark_count(const EngineArgs& a, uint32_t g) {
 // the launch must stop.  The copy waves poll the stripes themselves, so
 // the publisher is never on a copy's critical path; the engine's exit, and
 // so the completion check, come after every `ready` store.
-__device__ void publish_gates(const EngineArgs& a, uint64_t t0) {
+__device__ bool publish_gates(const EngineArgs& a, uint64_t t0) {
   const uint32_t lane = tc_lane_id();
   for (uint32_t spins = 0;;) {
     uint32_t shut = 0;
@@ -396,13 +471,59 @@ __device__ void publish_gates(const EngineArgs& a, uint64_t t0) {
         }
       }
     }
-    if (__all(shut == 0)) return;
-    if (wave_load_sys(a.force) != 0) return;
-    if (must_stop(a, t0, ++spins)) return;
+    if (__all(shut == 0)) return true;
+    if (wave_load_sys(a.force) != 0) return false;
+    if (must_stop(a, t0, ++spins)) return false;
     // Brisk polling: the engine cannot end before the publisher, so its pass
     // interval is on the round's critical path.
     __builtin_amdgcn_s_sleep(2);
   }
+}
+
+// The completion check, in the engine (the publisher runs it after its
+// gates): once every source's chunks are signalled, and only if the host has
+// asked (its producers are done, so their marks are all counted), the same
+// flags as the check kernel's, the engine status handed over, then the
+// sequence word.  Otherwise -- no request within kRequestPolls polls, or the
+// launch must stop -- it reports leaving unchecked through chk_exit, and the
+// host runs the check kernel instead.  Whole wave; chunks in lanes.
+constexpr uint32_t kRequestPolls = 48;
+
+__device__ void engine_check(const EngineArgs& a, uint64_t t0) {
+  const uint32_t lane = tc_lane_id();
+  bool checked = false;
+  for (uint32_t spins = 0;;) {  // every chunk signalled
+    bool ok = true;
+    if (lane < a.nranks)
+      ok = __hip_atomic_load(a.sig + lane * kTicketStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) >=
+           a.chunk_base[lane + 1] - a.chunk_base[lane];
+    if (__all(ok)) break;
+    if (must_stop(a, t0, ++spins)) goto leave;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  for (uint32_t polls = 0;; ++polls) {  // the host's request
+    if (wave_load_sys(a.chk_req) == a.chk_seq) break;
+    if (polls >= kRequestPolls) goto leave;
+    __builtin_amdgcn_s_sleep(16);
+  }
+  {
+    const CheckView v{a.chunks, a.gates, a.gate_stride, a.marks, a.nranks, a.round};
+    for (uint32_t g = lane; g < a.nchunks; g += 64)
+      __hip_atomic_store(a.chk_flags + g, check_chunk(v, g), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
+    const uint32_t st = wave_load_sys(a.status);
+    if (lane == 0) {
+      __hip_atomic_store(a.chk_status, st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      __hip_atomic_store(a.status, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    wave_wait_stores();
+    if (lane == 0)
+      __hip_atomic_store(a.chk_seq_host, a.chk_seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    checked = true;
+  }
+leave:
+  if (!checked && lane == 0)
+    __hip_atomic_store(a.chk_exit, a.launch_id, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 // The copy engine.  Every wave is an independent worker; all control flow is
@@ -427,7 +548,12 @@ __global__ __launch_bounds__(kEngineThreads) void engine_kernel(EngineArgs a) {
   // the GEMMs running beside the engine about 25%; the last CTA's costs
   // nothing measurable.)
   if (gw == gridDim.x * (kEngineThreads / 64) - 1) {
-    publish_gates(a, t0);
+    const bool all = publish_gates(a, t0);
+    if (a.chk_seq != 0) {
+      if (all) engine_check(a, t0);
+      else if (tc_lane_id() == 0)
+        __hip_atomic_store(a.chk_exit, a.launch_id, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
     return;
   }
   uint32_t acquired = 0xFFFFFFFFu;  // last chunk whose gate this wave has seen open
@@ -475,65 +601,12 @@ __global__ __launch_bounds__(kEngineThreads) void engine_kernel(EngineArgs a) {
   }
 }
 
-struct CheckArgs {
-  const ChunkD* chunks;
-  const uint8_t* gates;
-  uint64_t gate_stride;
-  const uint8_t* marks;
-  uint32_t* flags;        // mapped pinned host memory, one word per chunk
-  uint32_t* status;       // device engine status word: read, reported, cleared
-  uint32_t* status_host;  // mapped pinned host memory
-  uint32_t* seq_host;     // mapped pinned host memory: `seq` once every flag is written
-  uint32_t G, nranks, round, seq;
-};
-
-constexpr int kCheckThreads = 1024;
-
-__device__ inline uint64_t ld(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-
-// Flags of global chunk g: its counters against what a complete round r
-// leaves ([TP] Gates and rounds: this rank's chunk marked by all its writers
-// and arrived at every peer).
-__device__ uint32_t check_chunk(const CheckArgs& a, uint32_t g) {
-  const ChunkD cd = a.chunks[g];
-  const uint64_t want = (uint64_t)a.round * cd.writers;
-  uint64_t marks = 0;
-  for (uint32_t k = 0; k < TC_MARK_STRIPES; ++k)
-    marks += ld(reinterpret_cast<const uint64_t*>(
-        a.marks + ((uint64_t)g * TC_MARK_STRIPES + k) * TC_MARK_STRIPE_BYTES));
-  uint32_t f = 0;
-  if (marks > want) f |= kFlagExtra;
-  if (marks < want) f |= kFlagShortMarks;
-  for (uint32_t q = 0; q < a.nranks; ++q) {
-    const tc_gate_row* r = reinterpret_cast<const tc_gate_row*>(
-        a.gates + (uint64_t)q * a.gate_stride + (uint64_t)g * TC_GATE_ROW_BYTES);
-    for (int k = 0; k < 5; ++k)
-      if (ld(&r->rsvd[k]) != 0) f |= kFlagCorrupt;
-    if (ld(&r->writers) != 0) f |= kFlagCorrupt;
-    const uint64_t arr = ld(&r->arrival);
-    const uint64_t rdy = ld(&r->ready);
-    if (q == cd.rank) {
-      // The sender's row: no arrival; `ready` is this round once the gate
-      // has opened (it is stored before the chunk is signalled anywhere).
-      if (arr != 0 || rdy > a.round) f |= kFlagCorrupt;
-      if (rdy < a.round) f |= kFlagNotArrived;
-      continue;
-    }
-    if (rdy != 0) f |= kFlagCorrupt;
-    if (arr < a.round) f |= kFlagNotArrived;
-    if (arr > a.round) f |= kFlagCorrupt;
-  }
-  return f;
-}
-
 // One CTA: every chunk's flags into host memory, the engine's status handed
 // over (and cleared for the next launch), then the sequence number the host
 // waits for.
 __global__ __launch_bounds__(kCheckThreads) void check_kernel(CheckArgs a) {
   for (uint32_t g = threadIdx.x; g < a.G; g += kCheckThreads)
-    __hip_atomic_store(a.flags + g, check_chunk(a, g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(a.flags + g, check_chunk(a.v, g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   if (threadIdx.x == 0) {
     const uint32_t st = __hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     __hip_atomic_store(a.status_host, st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -648,6 +721,20 @@ static int launch_engine(tc_plan* P) {
   a.nranks = P->P;
   a.nchunks = P->G;
   a.launch_id = ++P->launch_id;
+  for (uint32_t p = 0; p <= P->P; ++p) a.chunk_base[p] = P->chunk_base[p];
+  // The completion check rides on this launch (the publisher runs it when
+  // wait() asks) unless the plan has no mapped host words, more chunks than
+  // a wave checks quickly, or is being closed.
+  P->engine_chk_seq = 0;
+  if (!P->noalloc && P->G <= kEngineCheckMaxChunks && !P->forced) {
+    P->engine_chk_seq = ++P->check_seq;
+    a.chk_seq = P->engine_chk_seq;
+    a.chk_req = P->req_dev;
+    a.chk_exit = P->exit_dev;
+    a.chk_flags = P->flags_dev;
+    a.chk_status = P->status_dev;
+    a.chk_seq_host = P->seq_dev;
+  }
   a.backstop_ticks = P->backstop_ticks;
   P->cur_launch_block = lb;
   P->launch_seq++;
@@ -691,21 +778,22 @@ static int order_engine_after(tc_plan* P, hipStream_t ps, hipEvent_t ev) {
 static int queue_check(tc_plan* P) {
   if (int rc = order_engine_after(P, P->producer_stream, P->ev_prod_end)) return rc;
   CheckArgs c{};
-  c.chunks = reinterpret_cast<const ChunkD*>(P->ws + P->L.chunks);
-  c.gates = P->ws + P->L.gates;
-  c.gate_stride = P->L.gate_stride;
-  c.marks = P->ws + P->L.marks;
+  c.v.chunks = reinterpret_cast<const ChunkD*>(P->ws + P->L.chunks);
+  c.v.gates = P->ws + P->L.gates;
+  c.v.gate_stride = P->L.gate_stride;
+  c.v.marks = P->ws + P->L.marks;
+  c.v.nranks = P->P;
+  c.v.round = P->round;
   c.flags = P->flags_dev;
   c.status = reinterpret_cast<uint32_t*>(P->ws + P->L.status);
   c.status_host = P->status_dev;
   c.seq_host = P->seq_dev;
   c.G = P->G;
-  c.nranks = P->P;
-  c.round = P->round;
   c.seq = ++P->check_seq;
   hipLaunchKernelGGL(check_kernel, dim3(1), dim3(kCheckThreads), 0, P->engine_stream, c);
   TC_HIP(hipGetLastError());
   TC_HIP(hipEventRecord(P->ev_check_done, P->engine_stream));  // for close()
+  P->check_queued = true;
   return TC_OK;
 }
 
@@ -748,6 +836,19 @@ static int check_done_by(tc_plan* P, uint32_t seq, std::chrono::steady_clock::ti
     } else if (__atomic_load_n(P->seq_host, __ATOMIC_ACQUIRE) == seq) {
       return 1;
     }
+    if (std::chrono::steady_clock::now() >= deadline) return 0;
+    if (++spins > 20000) std::this_thread::sleep_for(std::chrono::microseconds(20));
+  }
+}
+
+// After wait() asked the running engine for the completion check: 1 once
+// the check's sequence word is published, 2 once the engine reports that it
+// left without checking (the check kernel must run), 0 at the deadline.
+static int engine_check_by(const tc_plan* P, std::chrono::steady_clock::time_point deadline) {
+  int spins = 0;
+  for (;;) {
+    if (__atomic_load_n(P->seq_host, __ATOMIC_ACQUIRE) == P->engine_chk_seq) return 1;
+    if (__atomic_load_n(P->exit_host, __ATOMIC_ACQUIRE) == P->launch_id) return 2;
     if (std::chrono::steady_clock::now() >= deadline) return 0;
     if (++spins > 20000) std::this_thread::sleep_for(std::chrono::microseconds(20));
   }
@@ -872,6 +973,7 @@ static void destroy(tc_plan* P) {
     if (P->flags_host) (void)hipHostFree(P->flags_host);
     if (P->status_host) (void)hipHostFree(P->status_host);
     if (P->seq_host) (void)hipHostFree((void*)P->seq_host);
+    if (P->req_host) (void)hipHostFree((void*)P->req_host);
   }
   delete P;
 }
@@ -1013,6 +1115,14 @@ static int create_plan(const tc_plan_desc* d, uint8_t* ws, uint64_t ws_bytes,
     TC_HIP_C(hipHostMalloc((void**)&P->seq_host, 64, hipHostMallocMapped | hipHostMallocCoherent));
     *P->seq_host = 0;
     TC_HIP_C(hipHostGetDevicePointer((void**)&P->seq_dev, (void*)P->seq_host, 0));
+    // The in-engine check's request word (host writes) and exit note (the
+    // engine writes), 64 bytes apart.
+    TC_HIP_C(hipHostMalloc((void**)&P->req_host, 128, hipHostMallocMapped | hipHostMallocCoherent));
+    P->req_host[0] = 0;
+    P->req_host[16] = 0;
+    TC_HIP_C(hipHostGetDevicePointer((void**)&P->req_dev, (void*)P->req_host, 0));
+    P->exit_host = P->req_host + 16;
+    P->exit_dev = P->req_dev + 16;
   }
 
   // Zero the workspace (gates start at zero, [TP] Gates and rounds; a
@@ -1218,11 +1328,15 @@ int tc_plan_wait(tc_plan* P, uint64_t timeout_us) {
   // running meanwhile (GEMM producers beside the engine) by about 2%.  After
   // 1 ms the host sleeps 20 us between queries instead of spinning, so a long
   // producer does not hold a host core for the whole round.
+  bool drained = false;
   {
     const auto spin_until = std::chrono::steady_clock::now() + std::chrono::milliseconds(1);
     for (;;) {
       const hipError_t q = hipStreamQuery(P->producer_stream);
-      if (q == hipSuccess) break;
+      if (q == hipSuccess) {
+        drained = true;
+        break;
+      }
       if (q != hipErrorNotReady) return hip_fail(q, "hipStreamQuery(producer stream)");
       const auto now = std::chrono::steady_clock::now();
       if (now >= deadline) break;
@@ -1235,20 +1349,35 @@ int tc_plan_wait(tc_plan* P, uint64_t timeout_us) {
       }
     }
   }
-  if (int rc = queue_check(P)) return rc;
-  const uint32_t seq = P->check_seq;
-  const int first_check = check_done_by(P, seq, deadline);
-  if (first_check < 0) return first_check;
-  const bool timed_out = first_check == 0;
+  // The producer's work is done, so every mark it makes is counted: ask the
+  // engine's publisher for the check (it runs once every chunk is
+  // signalled), and fall back to the check kernel if the engine left
+  // without it.  Past the deadline the check kernel, ordered after the
+  // producer on the device, is the only way.
+  int in_engine = 0;
+  if (drained && P->engine_chk_seq && P->launch_id) {
+    __atomic_store_n(P->req_host, P->engine_chk_seq, __ATOMIC_SEQ_CST);
+    in_engine = engine_check_by(P, deadline);
+  }
+  P->engine_chk_seq = 0;
+  bool timed_out = false;
+  if (in_engine != 1) {
+    if (int rc = queue_check(P)) return rc;
+    const uint32_t seq = P->check_seq;
+    const int first_check = check_done_by(P, seq, deadline);
+    if (first_check < 0) return first_check;
+    timed_out = first_check == 0;
+  }
   if (timed_out) {
+    const uint32_t seq = P->check_seq;
     // Stop this launch of the engine if it still runs (every poll loop
     // watches the abort word), then let the queued check finish.
     if (hipEventQuery(P->ev_engine_done) != hipSuccess)
       if (int rc = set_abort(P)) return rc;
     const auto drain = std::chrono::steady_clock::now() + std::chrono::seconds(10);
-    const int drained = check_done_by(P, seq, drain);
-    if (drained < 0) return drained;
-    if (drained == 0) {
+    const int finished = check_done_by(P, seq, drain);
+    if (finished < 0) return finished;
+    if (finished == 0) {
       P->need_relaunch = hipEventQuery(P->ev_engine_done) == hipSuccess;
       return fail(TC_ETIMEOUT, "wait: the copy engine or the producer did not finish within 10 s "
                                "of the deadline");
@@ -1366,7 +1495,7 @@ int tc_plan_close(tc_plan* P, int* closing) {
       if (int rc = set_abort(P)) return rc;
       done = event_done_by(P->ev_engine_done, deadline(10), &err);
     }
-    if (done != 1 || (P->check_seq && event_done_by(P->ev_check_done, deadline(10), &err) != 1)) {
+    if (done != 1 || (P->check_queued && event_done_by(P->ev_check_done, deadline(10), &err) != 1)) {
       // Leak rather than free memory a kernel may still touch.
       return fail(TC_ETIMEOUT, "close: copy engine did not stop within 10 s");
     }

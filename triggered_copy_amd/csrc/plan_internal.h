@@ -77,7 +77,13 @@ struct tc_plan {
   uint32_t* status_dev = nullptr;
   volatile uint32_t* seq_host = nullptr;    // pinned, mapped: the last check's sequence number
   uint32_t* seq_dev = nullptr;
-  uint32_t check_seq = 0;
+  volatile uint32_t* req_host = nullptr;    // pinned, mapped: asks the engine for the check
+  uint32_t* req_dev = nullptr;
+  volatile uint32_t* exit_host = nullptr;   // pinned, mapped: the engine left without checking
+  uint32_t* exit_dev = nullptr;
+  uint32_t check_seq = 0;                   // last sequence number handed out
+  uint32_t engine_chk_seq = 0;              // the running launch's check number (0: none)
+  bool check_queued = false;                // a check kernel was ever queued (ev_check_done)
   bool noalloc = false;                     // workspace = the device's static array
   std::vector<uint32_t> flags_buf;          // no-allocation plan: the check's flags, copied back
   uint32_t status_word = 0;                 // no-allocation plan: the status word, copied back
