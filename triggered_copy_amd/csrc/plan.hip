@@ -738,11 +738,16 @@ static int launch_engine(tc_plan* P) {
   a.backstop_ticks = P->backstop_ticks;
   P->cur_launch_block = lb;
   P->launch_seq++;
-  if (P->engine_ms_pending) {  // read the previous launch's time before its events are reused
-    TC_HIP(hipEventSynchronize(P->ev_engine_done));
-    TC_HIP(hipEventElapsedTime(&P->last_engine_ms, P->ev_engine_start, P->ev_engine_done));
+  // Timing events alternate between two pairs, so a launch never waits for
+  // the previous one (still ending after wait() returned) to read its time:
+  // a pair is reused two launches later, and read then if still unread.
+  if (P->engine_ms_pending && P->pending_pair == lb) {
+    TC_HIP(hipEventSynchronize(P->ev_eng_done[lb]));
+    TC_HIP(hipEventElapsedTime(&P->last_engine_ms, P->ev_eng_start[lb], P->ev_eng_done[lb]));
     P->engine_ms_pending = false;
   }
+  P->ev_engine_start = P->ev_eng_start[lb];
+  P->ev_engine_done = P->ev_eng_done[lb];
   {
     Registry& R = registry();
     std::lock_guard<std::mutex> lock(R.mu);
@@ -959,8 +964,8 @@ static void destroy(tc_plan* P) {
     std::lock_guard<std::mutex> lock(R.mu);
     R.live.erase(std::remove(R.live.begin(), R.live.end(), P), R.live.end());
   }
-  for (hipEvent_t e : {P->ev_prod_start, P->ev_prod_end, P->ev_engine_start, P->ev_engine_done,
-                       P->ev_check_done})
+  for (hipEvent_t e : {P->ev_prod_start, P->ev_prod_end, P->ev_eng_start[0], P->ev_eng_done[0],
+                       P->ev_eng_start[1], P->ev_eng_done[1], P->ev_check_done})
     if (e) (void)hipEventDestroy(e);
   if (P->noalloc) {
     // The side stream and the workspace belong to the device, not the plan.
@@ -1087,8 +1092,12 @@ static int create_plan(const tc_plan_desc* d, uint8_t* ws, uint64_t ws_bytes,
   if (!P->noalloc) TC_HIP_C(hipStreamCreateWithFlags(&P->aux_stream, hipStreamNonBlocking));
   TC_HIP_C(hipEventCreateWithFlags(&P->ev_prod_start, hipEventDisableTiming));
   TC_HIP_C(hipEventCreateWithFlags(&P->ev_prod_end, hipEventDisableTiming));
-  TC_HIP_C(hipEventCreate(&P->ev_engine_start));
-  TC_HIP_C(hipEventCreate(&P->ev_engine_done));
+  for (int k = 0; k < 2; ++k) {
+    TC_HIP_C(hipEventCreate(&P->ev_eng_start[k]));
+    TC_HIP_C(hipEventCreate(&P->ev_eng_done[k]));
+  }
+  P->ev_engine_start = P->ev_eng_start[0];
+  P->ev_engine_done = P->ev_eng_done[0];
   TC_HIP_C(hipEventCreateWithFlags(&P->ev_check_done, hipEventDisableTiming));
   if (P->noalloc) {
     // The engine's abort word and the check's outputs live in the
@@ -1384,6 +1393,7 @@ int tc_plan_wait(tc_plan* P, uint64_t timeout_us) {
     }
   }
   P->engine_ms_pending = true;
+  P->pending_pair = P->cur_launch_block;
   const uint32_t st = __atomic_load_n(P->status_host, __ATOMIC_ACQUIRE);
   if (st & (kStatusAborted | kStatusExpired)) P->need_relaunch = true;
   bool extra = false, corrupt = false, shortc = false;
@@ -1633,9 +1643,10 @@ int tc_plan_read_cursors(tc_plan* P, uint32_t* host) {
 int tc_plan_stats(tc_plan* P, tc_stats* out) {
   if (!P || !out) return fail(TC_EINVAL, "stats: NULL argument");
   std::memset(out, 0, sizeof(*out));
-  if (P->engine_ms_pending) {  // the engine's events are complete once wait() saw the check
-    TC_HIP(hipEventSynchronize(P->ev_engine_done));
-    TC_HIP(hipEventElapsedTime(&P->last_engine_ms, P->ev_engine_start, P->ev_engine_done));
+  if (P->engine_ms_pending) {  // the launch that wait() saw through ends by itself
+    const uint32_t pp = P->pending_pair;
+    TC_HIP(hipEventSynchronize(P->ev_eng_done[pp]));
+    TC_HIP(hipEventElapsedTime(&P->last_engine_ms, P->ev_eng_start[pp], P->ev_eng_done[pp]));
     P->engine_ms_pending = false;
   }
   out->engine_ms = P->last_engine_ms;

@@ -67,7 +67,8 @@ struct tc_plan {
   hipStream_t aux_stream = nullptr;
   hipStream_t producer_stream = nullptr;
   hipEvent_t ev_prod_start = nullptr, ev_prod_end = nullptr;
-  hipEvent_t ev_engine_start = nullptr, ev_engine_done = nullptr;
+  hipEvent_t ev_eng_start[2] = {}, ev_eng_done[2] = {};  // alternating timing pairs
+  hipEvent_t ev_engine_start = nullptr, ev_engine_done = nullptr;  // the newest launch's pair
   hipEvent_t ev_check_done = nullptr;
   volatile uint32_t* abort_host = nullptr;  // pinned, mapped
   uint32_t* abort_dev = nullptr;
@@ -102,6 +103,7 @@ struct tc_plan {
   bool forced = false;       // close() has forced every gate open
   float last_engine_ms = 0.f;
   bool engine_ms_pending = false;  // last_engine_ms not yet read from the events
+  uint32_t pending_pair = 0;        // the pair holding that unread launch
   std::vector<uint32_t> problems;  // (rank, chunk) pairs
 };
 
