@@ -34,9 +34,16 @@ def common_flags():
             "-Wall", "-Wno-unused-function"]
 
 
+# Per-source flags.  The GEMM keeps its accumulators in ordinary VGPRs (the
+# VGPR form of the MFMA): with one wave per SIMD there is room, and the AGPR
+# form made the compiler copy accumulators between iterations of the K loop.
+EXTRA_FLAGS = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + common_flags()
+    cmd = ([hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + common_flags()
+           + EXTRA_FLAGS.get(src, []))
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)

@@ -16,18 +16,21 @@
 // rows, and before a step touches its 128-row block of A, the CTA waits
 // (tc_wait) for every chunk whose regions reach into those rows.
 //
-// gfx950 mapping: a 512-thread CTA computes a 128 x 128 tile with two groups
-// of 4 waves.  In each group the waves form a 2 x 2 grid of 64 x 64
-// sub-tiles, each 4 x 4 blocks of the 16x16x32 bf16 MFMA
-// (v_mfma_f32_16x16x32_bf16).  The groups split K: group g multiplies the
-// 64-wide slabs g, g + 2, g + 4, ..., each through two LDS buffers of its
-// own (slab k + 2 travels from global memory into registers and then into
-// the other buffer while slab k is multiplied).  Two waves per SIMD, one of
-// each group, so one wave's MFMAs cover the other's load and LDS latency.
-// At the end group 1 hands its partial sums to group 0 through LDS.  LDS
-// rows are padded by 16 bytes to spread the 16-byte fragment reads over the
-// banks; the finished tile is staged through LDS so the bf16 stores are
-// 16-byte vectors along the row.
+// gfx950 mapping: a 256-thread CTA computes a 128 x 128 tile; its 4 waves
+// form a 2 x 2 grid of 64 x 64 sub-tiles, each 4 x 4 blocks of the 16x16x32
+// bf16 MFMA (v_mfma_f32_16x16x32_bf16), and every wave runs the whole K
+// range, so no partial sums are exchanged.  Operands reach LDS without
+// passing through registers: buffer_load_dwordx4 with the LDS bit writes
+// each lane's 16 bytes to LDS at M0 + 16 * lane, and the 64-wide K slabs go
+// round a ring of kStages LDS buffers, so the loads for slabs k + 2 and
+// k + 3 are in flight while slab k + 1 waits its turn.  The lane -> global
+// address map is chosen so that the slab lands XOR-swizzled (16-byte column
+// c of row r at position c ^ (r % 8)), which spreads every fragment read
+// over all banks.  Rows past M and columns past K read as zero through the
+// buffer range check.  The first k step's fragments of the next slab are
+// read while the second k step of this slab is multiplied, so the matrix
+// cores see no gap at the slab barrier.  The finished tile is staged
+// through LDS so the bf16 stores are 16-byte vectors along the row.
 #include <hip/hip_runtime.h>
 
 #include <string>
@@ -44,12 +47,17 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDA = BK + 8;            // bf16 elements per LDS row (16 bytes of padding)
-constexpr int kThreads = 512;          // two groups of 4 waves
-constexpr int kGroupThreads = 256;
-constexpr int LDC = BN + 8;            // bf16 elements per staged C row
+constexpr int kThreads = 256;                  // 4 waves
+constexpr int kStages = 4;                     // LDS ring depth, in K slabs
+constexpr int kRowBytes = BK * 2;              // one slab row: 8 columns of 16 bytes
+constexpr int kOpBytes = BM * kRowBytes;       // one operand's slab: 16 KiB
+constexpr int kStageBytes = 2 * kOpBytes;      // A slab, then B slab
+constexpr int kLoads = kOpBytes / (kThreads * 16);  // LDS-DMA loads per thread per operand
+constexpr int LDC = BN + 8;                    // bf16 elements per staged C row
+constexpr uint32_t kNoRead = 0x80000000u;      // a buffer offset past every range: reads 0
 
 struct GemmArgs {
   const uint16_t* A;
@@ -75,28 +83,58 @@ __device__ inline uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int n>
+__device__ inline void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One 16-byte LDS-DMA load per lane: buffer_load_dwordx4 with the LDS bit
+// reads rsrc at voff and writes lane l's 16 bytes to LDS at m0 + 16 l.  It
+// is written out by hand so that the compiler, which cannot tell which ring
+// buffer a DMA fills, does not wait for every DMA in flight before each LDS
+// read; the kernel waits for them itself (vmcnt counts these loads).
+__device__ inline void lds_dma16(u32x4 rsrc, uint32_t voff, uint32_t m0) {
+  asm volatile(
+      "s_nop 0\n\t"  // one wait state between the write of m0 and its use here
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "{m0}"(m0)
+      : "memory");
+}
+
+// A raw buffer descriptor (stride 0) over [base, base + bytes).
+__device__ inline u32x4 buffer_desc(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  return u32x4{tc_uniform((uint32_t)p), tc_uniform((uint32_t)(p >> 32) & 0xFFFFu), tc_uniform(bytes),
+               0x00020000u};
+}
+
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
-  // LDS: slab (group g, buffer b, operand o) at (4 g + 2 b + o) * kSlab during
-  // the K loop; afterwards group 1's partial sums (kRed floats) followed by
-  // the staged C tile.
-  constexpr int kSlab = BM * LDA;        // bf16 elements per operand slab
-  constexpr int kVecPerRow = BK / 8;     // 16-byte vectors per slab row
-  constexpr int kVec = BM * kVecPerRow / kGroupThreads;  // vectors per thread per operand
-  constexpr int kRed = 4 * 64 * 64;      // floats: 4 waves x 64 lanes x 64 accumulators
-  static_assert(BM == BN && BM * kVecPerRow % kGroupThreads == 0, "slab vectors split evenly");
-  static_assert(8 * kSlab * 2 >= kRed * 4 + BM * LDC * 2, "reduction and C staging fit");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[8 * kSlab];
-  float* red = reinterpret_cast<float*>(lds);
-  uint16_t* cst = lds + kRed * 2;
+  static_assert(kStages * kStageBytes >= BM * LDC * 2, "C staging fits in the ring");
+  static_assert(kOpBytes % (kThreads * 16) == 0 && kLoads * 4 * 64 * 16 == kOpBytes,
+                "every wave loads whole 1 KiB blocks");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStageBytes];
+  uint16_t* cst = reinterpret_cast<uint16_t*>(lds);
+  const uint32_t lds_base = tc_uniform((uint32_t)(uintptr_t)(lds_ptr_t)lds);
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
-  const uint32_t grp = tc_uniform(tid >> 8);           // K group, wave-uniform
-  const uint32_t gw = tc_uniform((tid >> 6) & 3);      // wave within the group
-  const uint32_t gtid = tid & (kGroupThreads - 1);
-  const uint32_t wm = gw >> 1, wn = gw & 1;
+  const uint32_t wave = tc_uniform(tid >> 6);
+  const uint32_t wm = wave >> 1, wn = wave & 1;
   const uint32_t nk = (a.K + BK - 1) / BK;
-  const uint32_t niter = (nk + 1) / 2;                 // slabs per group, rounded up
+
+  // Loads: wave w, load i of an operand fills the 1 KiB block of slab rows
+  // 8 (kLoads w + i) .. +7; lane l lands at row + l / 8, position l % 8,
+  // which holds the row's 16-byte column (l % 8) ^ (l / 8).
+  const uint32_t lrow = lane >> 3, lcol = (lane & 7) ^ lrow;
+  // Fragment reads: lane l of a 16x16x32 block holds row l % 16 and the 8 k
+  // values of 16-byte column 4 h + l / 16 (k step h of the slab).
+  const uint32_t fr = lane & 15, fq = lane >> 4;
+  const uint32_t a_frag = (wm * 64 + fr) * kRowBytes, b_frag = kOpBytes + (wn * 64 + fr) * kRowBytes;
+  const uint32_t xcol0 = ((0 + fq) ^ (fr & 7)) * 16, xcol1 = ((4 + fq) ^ (fr & 7)) * 16;
 
   // Workgroups are dealt to the 8 XCDs round-robin; program p of the
   // persistent grid is workgroup w(p) such that each XCD runs consecutive
@@ -108,43 +146,56 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
   for (uint32_t step = first; step < a.tiles; step += gridDim.x) {
     const uint32_t t = tc_tile_of(step, a.tm, a.tn, a.group_m);
     const uint32_t m0 = (t / a.tn) * BM, n0 = (t % a.tn) * BN;
+    const uint32_t rows_in = a.M - m0 < (uint32_t)BM ? a.M - m0 : (uint32_t)BM;
+    const uint32_t cols_in = a.N - n0 < (uint32_t)BN ? a.N - n0 : (uint32_t)BN;
+
+    // Each operand's tile rows through a buffer resource whose range ends
+    // with the last valid row's K elements: rows past M or N read as zero.
+    const u32x4 ra = buffer_desc(a.A + (uint64_t)m0 * a.lda,
+                                 (uint32_t)(((uint64_t)(rows_in - 1) * a.lda + a.K) * 2));
+    const u32x4 rb = buffer_desc(a.Bt + (uint64_t)n0 * a.K, (uint32_t)((uint64_t)cols_in * a.K * 2));
+    uint32_t offa[kLoads], offb[kLoads];
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const uint32_t r = 8 * (kLoads * wave + i) + lrow;
+      offa[i] = (uint32_t)(r * a.lda * 2) + lcol * 16;
+      offb[i] = (uint32_t)(r * a.K * 2) + lcol * 16;
+    }
+    // Part i of slab kt's loads into ring buffer b: load i of each operand.
+    // Columns past K (a ragged last slab, or a slab past the end) read as
+    // zero: every offset stays below 2^31 (a tile spans less than 2 GiB),
+    // so setting bit 31 moves it past the range.
+    auto issue_part = [&](uint32_t kt, uint32_t b, int i) {
+      const uint32_t kmask = kt * BK + lcol * 8 < a.K ? 0u : kNoRead;
+      const uint32_t kb = kt * kRowBytes;
+      const uint32_t base = lds_base + b * kStageBytes + wave * kLoads * 1024 + i * 1024;
+      lds_dma16(ra, (offa[i] + kb) | kmask, base);
+      lds_dma16(rb, (offb[i] + kb) | kmask, base + kOpBytes);
+    };
+    // Group g of one k step's 8 fragment reads: the B fragments (output
+    // columns 16 j.. of this wave's 64) in groups 0 and 1, the A fragments
+    // (rows 16 i..) in groups 2 and 3.  A row of MFMAs needs all of B and
+    // one A fragment, so rows 0 and 1 can start once group 2 has landed.
+    auto read_group = [&](uint32_t b, uint32_t xcol, int g, bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
+      const uint8_t* s = lds + b * kStageBytes;
+      bf16x8* f = g < 2 ? fb : fa;
+      const uint32_t base = g < 2 ? b_frag : a_frag;
+      const int i0 = 2 * (g & 1);
+      f[i0] = *reinterpret_cast<const bf16x8*>(s + base + i0 * 16 * kRowBytes + xcol);
+      f[i0 + 1] = *reinterpret_cast<const bf16x8*>(s + base + (i0 + 1) * 16 * kRowBytes + xcol);
+    };
 
     f32x4 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // Vector v = gtid + 256 * s of a slab covers row v / kVecPerRow, k
-    // columns 8 * (v % kVecPerRow) .. +7; rows and k past the matrix read
-    // as zero.
-    u32x4 ra[kVec], rb[kVec];
-    auto fetch = [&](uint32_t kt) {
-      const uint32_t k0 = kt * BK;
+    // Row i of the 4 x 4 blocks for one k step.  The B fragment goes first,
+    // so each output block is C transposed.
+    auto mfma_row = [&](int i, const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
 #pragma unroll
-      for (int s = 0; s < kVec; ++s) {
-        const uint32_t v = gtid + kGroupThreads * s;
-        const uint32_t r = v / kVecPerRow, kc = k0 + (v % kVecPerRow) * 8;
-        const bool kin = kc < a.K;
-        ra[s] = (m0 + r < a.M && kin)
-                    ? *reinterpret_cast<const u32x4*>(a.A + (uint64_t)(m0 + r) * a.lda + kc)
-                    : u32x4{0, 0, 0, 0};
-        rb[s] = (n0 + r < a.N && kin)
-                    ? *reinterpret_cast<const u32x4*>(a.Bt + (uint64_t)(n0 + r) * a.K + kc)
-                    : u32x4{0, 0, 0, 0};
-      }
-    };
-    auto slab = [&](uint32_t buf) { return lds + (4 * grp + 2 * buf) * kSlab; };
-    auto stash = [&](uint32_t buf) {
-      uint16_t* As = slab(buf);
-      uint16_t* Bs = As + kSlab;
-#pragma unroll
-      for (int s = 0; s < kVec; ++s) {
-        const uint32_t v = gtid + kGroupThreads * s;
-        const uint32_t r = v / kVecPerRow, c = (v % kVecPerRow) * 8;
-        *reinterpret_cast<u32x4*>(As + r * LDA + c) = ra[s];
-        *reinterpret_cast<u32x4*>(Bs + r * LDA + c) = rb[s];
-      }
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
     };
 
     if (a.wait) {
@@ -158,87 +209,85 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
           ok = false;
       if (!ok && a.status && tc_is_cta_leader()) a.status[b] = 2u;
     }
-    __syncthreads();  // the previous tile's partial sums and C staging are no longer read
-    if (grp < nk) {
-      fetch(grp);
-      stash(0);
-    }
+    __syncthreads();  // the previous tile's C staging is no longer read
+    // The ring holds slabs kt - 1 .. kt + 2.  At the barrier in the middle
+    // of iteration kt every wave is done with slab kt - 1, whose buffer then
+    // takes slab kt + 3.  Every iteration issues one slab, past the end too
+    // (those read as zero into a buffer no one reads), so when slab kt + 1
+    // is waited for, exactly one slab follows it.  (Refilling slab kt's own
+    // buffer at that barrier, one more slab in flight, measured slower.)
+    static_assert(kStages == 4, "the waits below count one slab in flight behind the next");
+    constexpr int kSlabLoads = 2 * kLoads;  // one slab's loads per wave
+    for (uint32_t s = 0; s + 1 < kStages; ++s)
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) issue_part(s, s, i);
+    wait_vmcnt<2 * kSlabLoads>();  // slab 0 has landed; slabs 1 and 2 may be in flight
     __syncthreads();
-    // Every wave passes the same barriers: a group without a slab in some
-    // iteration (odd slab counts) skips the work, not the barrier.
-    for (uint32_t it = 0; it < niter; ++it) {
-      const uint32_t kt = 2 * it + grp, cur = it & 1;
-      if (kt + 2 < nk) fetch(kt + 2);  // in flight while this slab is multiplied
-      if (kt < nk) {
-        // Operand fragment of one 16x16x32 block: lane l holds row (l % 16)
-        // and 8 consecutive k values starting at 8 * (l / 16).  Both 32-wide
-        // k steps' fragments are read first, then the 32 MFMAs run (the
-        // scheduling barrier keeps the compiler from interleaving them back
-        // into read-wait-multiply pairs); the other wave of the SIMD covers
-        // this wave's LDS latency.
-        const uint16_t* As = slab(cur);
-        const uint16_t* Bs = As + kSlab;
-        const uint32_t fr = lane & 15, fq = 8 * (lane >> 4);
-        bf16x8 fa[2][4], fb[2][4];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            fa[h][i] = *reinterpret_cast<const bf16x8*>(As + (wm * 64 + i * 16 + fr) * LDA + 32 * h + fq);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            fb[h][j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 64 + j * 16 + fr) * LDA + 32 * h + fq);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[h][j], fa[h][i], acc[i][j], 0, 0, 0);
-      }
-      // The other buffer was last read in the previous iteration, which every
-      // wave finished before that iteration's closing barrier.
-      if (kt + 2 < nk) stash(cur ^ 1);
-      __syncthreads();
-    }
 
-    // Group 1's partial sums to LDS, in the same fragment order group 0's
-    // wave of the same (wm, wn) holds them.
-    if (grp == 1) {
+    // Each k step's MFMAs run while the next k step's fragments are read:
+    // the first row of four MFMAs goes out, then all 8 reads for the next k
+    // step, then the other three rows, so the reads have a whole k step to
+    // land; after the slab barrier the next slab's loads follow the rows.
+    // The scheduling barriers keep the compiler from regrouping them.
+    bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int g = 0; g < 4; ++g) read_group(0, xcol0, g, fa0, fb0);
+    uint32_t kt = 0;
+    for (; kt + 1 < nk; ++kt) {
+      const uint32_t cur = kt % kStages, nxt = (kt + 1) % kStages;
+      const uint32_t fill = (kt + kStages - 1) % kStages;
+      mfma_row(0, fa0, fb0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<f32x4*>(red + ((gw * 16 + i * 4 + j) * 64 + lane) * 4) = acc[i][j];
+      for (int g = 0; g < 4; ++g) read_group(cur, xcol1, g, fa1, fb1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 1; i < 4; ++i) mfma_row(i, fa0, fb0);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<kSlabLoads>();  // slab kt + 1 has landed for this wave
+      __syncthreads();
+      mfma_row(0, fa1, fb1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) read_group(nxt, xcol0, g, fa0, fb0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        issue_part(kt + kStages - 1, fill, i);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i < 3) mfma_row(i + 1, fa1, fb1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    __syncthreads();
-    // Group 0 adds them and stages the tile as bf16.  The MFMA takes the B
-    // fragment as its first operand, so its output block is C transposed:
-    // lane l holds row l % 16 and the 4 consecutive columns 4 * (l / 16) + e,
-    // e = 0..3 -- one 8-byte write per block.
-    if (grp == 0) {
+    mfma_row(0, fa0, fb0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int g = 0; g < 4; ++g) read_group(kt % kStages, xcol1, g, fa1, fb1);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4 o = *reinterpret_cast<const f32x4*>(red + ((gw * 16 + i * 4 + j) * 64 + lane) * 4);
-          const uint32_t r = wm * 64 + i * 16 + (lane & 15);
-          const uint32_t c = wn * 64 + j * 16 + 4 * (lane >> 4);
-          const uint32_t lo = f32_to_bf16_rne(acc[i][j][0] + o[0]) | (f32_to_bf16_rne(acc[i][j][1] + o[1]) << 16);
-          const uint32_t hi = f32_to_bf16_rne(acc[i][j][2] + o[2]) | (f32_to_bf16_rne(acc[i][j][3] + o[3]) << 16);
-          *reinterpret_cast<uint2*>(cst + r * LDC + c) = make_uint2(lo, hi);
-        }
-    }
+    for (int i = 1; i < 4; ++i) mfma_row(i, fa0, fb0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mfma_row(i, fa1, fb1);
+    wait_vmcnt<0>();  // the loads past the end, before the ring is reused
+    __syncthreads();  // every wave is done with the ring
+
+    // Stage the tile as bf16.  The MFMA output block is C transposed: lane l
+    // holds row l % 16 and the 4 consecutive columns 4 * (l / 16) + e --
+    // one 8-byte write per block.
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t r = wm * 64 + i * 16 + fr;
+        const uint32_t c = wn * 64 + j * 16 + 4 * fq;
+        const uint32_t lo = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
+        const uint32_t hi = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
+        *reinterpret_cast<uint2*>(cst + r * LDC + c) = make_uint2(lo, hi);
+      }
     __syncthreads();
-    // 128 rows x 16 vectors of 8 bf16: 4 vectors per thread, stored through
+    // 128 rows x 16 vectors of 8 bf16: 8 vectors per thread, stored through
     // to memory at system scope, so that once they complete the tile is
     // visible everywhere and mark_ready needs no L2 write-back.  Lanes
     // outside the matrix get an offset past the buffer range and their
     // stores are dropped.
-    const uint32_t rows_in = a.M - m0 < (uint32_t)BM ? a.M - m0 : (uint32_t)BM;
-    const uint32_t cols_in = a.N - n0 < (uint32_t)BN ? a.N - n0 : (uint32_t)BN;
     const uint32_t extent = (uint32_t)(((uint64_t)(rows_in - 1) * a.ldc + cols_in) * 2);
     const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
         a.C + (uint64_t)m0 * a.ldc + n0, 0, (int)extent, 0x00020000);
@@ -266,8 +315,9 @@ static int check_gemm_shape(const void* A, const void* Bt, const void* C, uint32
   if (K % 8 || N % 8 || ldc % 8 || ldc < N || lda % 8 || lda < K)
     return fail(TC_EINVAL, "gemm: K, N, lda and ldc must be multiples of 8 (16-byte rows), "
                            "lda >= K, ldc >= N");
-  if ((uint64_t)BM * ldc * 2 >= (1ull << 31))
-    return fail(TC_EINVAL, "gemm: a 128-row tile of C must span less than 2 GiB (ldc < 2^23)");
+  if ((uint64_t)BM * ldc * 2 >= (1ull << 31) || (uint64_t)BM * lda * 2 >= (1ull << 31))
+    return fail(TC_EINVAL, "gemm: a 128-row tile of A or C must span less than 2 GiB "
+                           "(lda, ldc < 2^23)");
   if (((uintptr_t)A | (uintptr_t)Bt | (uintptr_t)C) & 15)
     return fail(TC_EINVAL, "gemm: operands must be 16-byte aligned");
   int dev = 0;
