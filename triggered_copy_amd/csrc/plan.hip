@@ -210,11 +210,16 @@ __device__ inline bool must_stop(const EngineArgs& a, uint64_t t0, uint32_t spin
 }
 
 // How a waiting wave backs off between polls.  Gate polls by most waves of a
-// large grid are "reserve" polls: about 20 us between polls once the wave
-// has waited a little, so thousands of idle workers put almost no load on
-// the memory system while a producer runs.  The few waves waiting on another
-// wave of the engine (a chunk's last pieces, its turn to signal) poll
-// briskly: they are on the round's critical path.
+// large grid are "reserve" polls: about 7 us between polls once the wave has
+// waited a little, so thousands of idle workers put little load on the
+// memory system while a producer runs.  (20 us measured slower on 8-rank
+// rounds of whole chunks: a chunk waits for the last of its pieces' waves
+// to wake.)  Other gate polls ("normal") come 0.4 us apart for the first 16,
+// then about 7 us apart: a short producer is caught at once, a long one (a
+// GEMM) is not slowed by the polling.  The few
+// waves waiting on another wave of the engine (a chunk's last pieces, its
+// turn to signal) poll briskly: they are on the round's critical path.  The
+// mode must be a scalar (wave-uniform) value: see gate_mode.
 constexpr int kPollNormal = 0, kPollReserve = 1, kPollBrisk = 2;
 
 // The pause after the spins-th fruitless poll in a row.
@@ -222,10 +227,14 @@ __device__ inline void backoff(int mode, uint32_t spins) {
   if (spins < 8 || mode == kPollBrisk) {
     __builtin_amdgcn_s_sleep(1);
   } else if (mode == kPollNormal) {
-    if (spins < 64) __builtin_amdgcn_s_sleep(16);
-    else __builtin_amdgcn_s_sleep(64);
+    if (spins < 16) {
+      __builtin_amdgcn_s_sleep(16);
+    } else {
+      __builtin_amdgcn_s_sleep(127);
+      __builtin_amdgcn_s_sleep(127);
+    }
   } else {
-    for (int k = 0; k < 6; ++k) __builtin_amdgcn_s_sleep(127);
+    for (int k = 0; k < 2; ++k) __builtin_amdgcn_s_sleep(127);
   }
 }
 
@@ -241,18 +250,6 @@ __device__ inline bool poll_until(const EngineArgs& a, uint64_t t0, int mode, Re
     if (must_stop(a, t0, ++spins)) return false;
     backoff(mode, spins);
   }
-}
-
-// The mark count of global chunk g: the sum of its stripes.  Uniform.
-__device__ inline uint64_t mark_count(const EngineArgs& a, uint32_t g) {
-  const uint64_t* s = reinterpret_cast<const uint64_t*>(a.marks + (uint64_t)g * TC_MARK_STRIPES *
-                                                                       TC_MARK_STRIPE_BYTES);
-  uint64_t sum = 0;
-#pragma unroll
-  for (uint32_t k = 0; k < TC_MARK_STRIPES; ++k)
-    sum += tc_uniform64(__hip_atomic_load(s + k * (TC_MARK_STRIPE_BYTES / 8), __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT));
-  return sum;
 }
 
 __device__ inline tc_gate_row* gate_row(const EngineArgs& a, uint32_t table, uint32_t g) {
@@ -558,8 +555,11 @@ __global__ __launch_bounds__(kEngineThreads) void engine_kernel(EngineArgs a) {
   }
   uint32_t acquired = 0xFFFFFFFFu;  // last chunk whose gate this wave has seen open
   // Large grids keep one wave in eight polling briskly and let the rest back
-  // off; small grids poll with every wave.
-  const int gate_mode = gridDim.x >= 256 && gw % 8 != 0 ? kPollReserve : kPollNormal;
+  // off; small grids poll with every wave.  The mode is read back as a scalar
+  // so that backoff() branches on it: lowered as a per-lane branch with no
+  // skip, the reserve sleeps (scalar instructions, which run whatever the
+  // lane mask) would be taken in every mode.
+  const int gate_mode = (int)tc_uniform(gridDim.x >= 256 && gw % 8 != 0 ? kPollReserve : kPollNormal);
 
   for (uint32_t s = 0; s < a.nranks; ++s) {
     const uint32_t p = (gw + s) % a.nranks;
@@ -572,10 +572,20 @@ __global__ __launch_bounds__(kEngineThreads) void engine_kernel(EngineArgs a) {
       const uint32_t g = tc_uniform(pc.chunk);
       if (g != acquired) {
         // The gate of round r is open once the chunk's marks reach r * writers
-        // (or once close() forces every gate of the plan open).
-        const uint64_t want = (uint64_t)a.round * tc_uniform(a.chunks[g].writers);
-        if (!poll_until(a, t0, gate_mode,
-                        [&] { return mark_count(a, g) >= want || wave_load_sys(a.force) != 0; }))
+        // (or once close() forces every gate of the plan open).  Waiting
+        // waves read the one `ready` word the publisher stores when it sees
+        // the count complete, not the stripes: a poll is then one load (and
+        // the force word one poll in 16).  Hundreds of waves polling nine
+        // words each at short intervals made the memory channels holding
+        // them hot enough to slow GEMM producers running beside the engine
+        // by about 30%.
+        const uint64_t* ready = &gate_row(a, a.chunks[g].rank, g)->ready;
+        uint32_t polls = 0;
+        if (!poll_until(a, t0, gate_mode, [&] {
+              return tc_uniform64(__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)) >=
+                         a.round ||
+                     (++polls % 16 == 0 && wave_load_sys(a.force) != 0);
+            }))
           return;
         // The wave holding a chunk's first piece records when it saw the gate open.
         if (a.piece_base[p] + t == a.chunks[g].first_piece) wave_max32(&a.stats[0], ~(uint32_t)now_ticks());
