@@ -190,6 +190,17 @@ def run_headline(args, torch, tc, workloads, seed):
     return out
 
 
+def overlap_mask(torch, ncus):
+    """CU mask words selecting the first `ncus` CUs for the engine (None: all)."""
+    if not ncus:
+        return None
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    mask = [0] * ((ncu + 31) // 32)
+    for i in range(min(ncus, ncu)):
+        mask[i // 32] |= 1 << (i % 32)
+    return mask
+
+
 def run_overlap(torch, tc, workloads, seed, reps=40, cu_mask=None, engine_ctas=0):
     """GEMM producer time for P ranks back to back, without any plan and with
     the copy engine delivering each rank's tiles while the next GEMM runs."""
@@ -666,8 +677,10 @@ def main():
         print(json.dumps(run_gemm_only(torch, tc, workloads, BASE_SEED, args.steps)), flush=True)
         return
     if args.overlap_only:
-        print(json.dumps(run_overlap(torch, tc, workloads, BASE_SEED,
-                                     engine_ctas=args.overlap_engine_ctas)), flush=True)
+        r = run_overlap(torch, tc, workloads, BASE_SEED, cu_mask=overlap_mask(torch, args.overlap_cus),
+                        engine_ctas=args.overlap_engine_ctas)
+        r["engine_cus"] = args.overlap_cus or "all"
+        print(json.dumps(r), flush=True)
         return
 
     if args.calibrate:
@@ -688,15 +701,16 @@ def main():
     extras = {}
     if not args.no_extras:
         log("overlap: 4 GEMM producers with and without the copy engine")
-        mask = None
-        if args.overlap_cus:
-            ncu = torch.cuda.get_device_properties(0).multi_processor_count
-            mask = [0] * ((ncu + 31) // 32)
-            for i in range(min(args.overlap_cus, ncu)):
-                mask[i // 32] |= 1 << (i % 32)
-        extras["gemm_overlap"] = run_overlap(torch, tc, workloads, BASE_SEED, cu_mask=mask,
+        extras["gemm_overlap"] = run_overlap(torch, tc, workloads, BASE_SEED,
+                                             cu_mask=overlap_mask(torch, args.overlap_cus),
                                              engine_ctas=args.overlap_engine_ctas)
         extras["gemm_overlap"]["engine_cus"] = args.overlap_cus or "all"
+        # The same rounds with a larger engine (160 CTAs): a shorter round for
+        # about the same producer slowdown.
+        log("overlap: the same with 160 engine CTAs")
+        extras["gemm_overlap_160"] = run_overlap(torch, tc, workloads, BASE_SEED,
+                                                 cu_mask=overlap_mask(torch, args.overlap_cus),
+                                                 engine_ctas=160)
         log("in-kernel consumers: after wait() vs waiting on the device")
         extras["gemm_consumer"] = run_consumer_overlap(torch, tc, workloads, BASE_SEED)
         log("barrier: 8 ranks x 1000 generations")
