@@ -210,16 +210,17 @@ __device__ inline bool must_stop(const EngineArgs& a, uint64_t t0, uint32_t spin
 }
 
 // How a waiting wave backs off between polls.  Gate polls by most waves of a
-// large grid are "reserve" polls: about 7 us between polls once the wave has
-// waited a little, so thousands of idle workers put little load on the
-// memory system while a producer runs.  (20 us measured slower on 8-rank
-// rounds of whole chunks: a chunk waits for the last of its pieces' waves
-// to wake.)  Other gate polls ("normal") come 0.4 us apart for the first 16,
-// then about 7 us apart: a short producer is caught at once, a long one (a
-// GEMM) is not slowed by the polling.  The few
-// waves waiting on another wave of the engine (a chunk's last pieces, its
-// turn to signal) poll briskly: they are on the round's critical path.  The
-// mode must be a scalar (wave-uniform) value: see gate_mode.
+// large grid are "reserve" polls: about 3.4 us between polls once the wave
+// has waited a little, so thousands of idle workers put little load on the
+// memory system while a producer runs.  (7 and 20 us measured slower on
+// 8-rank rounds of whole chunks, 110.5 and 125-128 us p90 against 106.6: a
+// chunk waits for the last of its pieces' waves to wake.)  Other gate polls
+// ("normal") come 0.4 us apart for the first 16, then about 7 us apart: a
+// short producer is caught at once, a long one (a GEMM) is not slowed by the
+// polling.  The few waves waiting on another wave of the engine (a chunk's
+// last pieces, its turn to signal) poll briskly: they are on the round's
+// critical path.  The mode must be a scalar (wave-uniform) value: see
+// gate_mode.
 constexpr int kPollNormal = 0, kPollReserve = 1, kPollBrisk = 2;
 
 // The pause after the spins-th fruitless poll in a row.
@@ -234,7 +235,7 @@ __device__ inline void backoff(int mode, uint32_t spins) {
       __builtin_amdgcn_s_sleep(127);
     }
   } else {
-    for (int k = 0; k < 2; ++k) __builtin_amdgcn_s_sleep(127);
+    __builtin_amdgcn_s_sleep(127);
   }
 }
 
@@ -1183,6 +1184,21 @@ static int create_plan(const tc_plan_desc* d, uint8_t* ws, uint64_t ws_bytes,
   TC_HIP_C(hipMemcpyAsync(P->ws + P->L.wprefix, wprefix.data(), wprefix.size() * 8,
                           hipMemcpyHostToDevice, P->aux_stream));
   TC_HIP_C(hipStreamSynchronize(P->aux_stream));  // the host arrays above are about to go
+
+  // Longest byte range one writer of a contiguous chunk covers (the parallel
+  // fill writes such a share with one write-through span when it fits).
+  P->max_range_share = 0;
+  for (const ChunkD& c : P->chunks) {
+    if (!(c.flags & kChunkContiguous)) continue;
+    for (uint32_t j = 0; j < c.writers; ++j) {
+      const uint64_t lo = (uint64_t)j * c.npieces / c.writers;
+      const uint64_t hi = (uint64_t)(j + 1) * c.npieces / c.writers;
+      if (lo == hi) continue;
+      const PieceD& a = P->pieces[c.first_piece + lo];
+      const PieceD& b = P->pieces[c.first_piece + hi - 1];
+      P->max_range_share = std::max(P->max_range_share, b.off + b.row_bytes - a.off);
+    }
+  }
 
   // One-shot fill table, when every chunk is one byte range: each writer's
   // share cut into kOneShotBlock blocks, every rank's chunk 0 first, then

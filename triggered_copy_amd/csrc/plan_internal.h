@@ -61,6 +61,7 @@ struct tc_plan {
   uint64_t total_writers = 0;
   uint64_t bytes_read = 0, bytes_moved = 0;
   uint64_t oneshot_blocks = 0;  // one-shot fill grid (0: some chunk is not one byte range)
+  uint64_t max_range_share = 0; // longest byte range of one writer of a contiguous chunk
 
   int device = 0;
   hipStream_t engine_stream = nullptr;

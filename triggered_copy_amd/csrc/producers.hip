@@ -121,7 +121,7 @@ __device__ void fill_span(const FillArgs& a, uint32_t p, uint64_t off, uint64_t 
     const uint32_t per = 16 / e;  // elements per 16-byte vector
     const uint64_t nv = len / 16;
     u32x4* dst = reinterpret_cast<u32x4*>(base + off);
-    for (uint64_t v = threadIdx.x; v < nv; v += kFillThreads) {
+    auto value = [&](uint64_t v) {
       const uint64_t i0 = idx0 + v * per;
       u32x4 out;
       if (a.kind == TC_FILL_U32) {
@@ -141,11 +141,28 @@ __device__ void fill_span(const FillArgs& a, uint32_t p, uint64_t off, uint64_t 
           out[k] = w;
         }
       }
+      return out;
+    };
+    auto put = [&](uint64_t v, const u32x4& out) {
       if (kWriteThrough)
         __builtin_amdgcn_raw_buffer_store_b128(out, wt, (int)(v * 16), 0, 17 /* sc0 sc1 */);
       else
         dst[v] = out;
+    };
+    // Four vectors per thread per pass: their hash chains are independent,
+    // so one wave per SIMD keeps the arithmetic units busy (a CTA of more
+    // waves might not fit beside a persistent copy engine that fills the
+    // CU's other slots, and must run while it waits for the marks).
+    uint64_t v = threadIdx.x;
+    for (; v + 3 * kFillThreads < nv; v += 4 * kFillThreads) {
+      const u32x4 o0 = value(v), o1 = value(v + kFillThreads), o2 = value(v + 2 * kFillThreads),
+                  o3 = value(v + 3 * kFillThreads);
+      put(v, o0);
+      put(v + kFillThreads, o1);
+      put(v + 2 * kFillThreads, o2);
+      put(v + 3 * kFillThreads, o3);
     }
+    for (; v < nv; v += kFillThreads) put(v, value(v));
   } else {
     const uint64_t n = len / e;
     uint8_t* d = base + off;
@@ -167,29 +184,37 @@ __device__ void fill_span(const FillArgs& a, uint32_t p, uint64_t off, uint64_t 
   }
 }
 
+template <bool kWriteThrough = false>
 __device__ void fill_range(const FillArgs& a, uint32_t p, uint64_t off, uint64_t len) {
-  fill_span<false>(a, p, off, len, index_at(a, p, off));
+  fill_span<kWriteThrough>(a, p, off, len, index_at(a, p, off));
 }
 
+template <bool kWriteThrough = false>
 __device__ void fill_piece(const FillArgs& a, uint32_t p, const tc::PieceD& pc) {
-  for (uint32_t r = 0; r < pc.rows; ++r) fill_range(a, p, pc.off + (uint64_t)r * pc.pitch, pc.row_bytes);
+  for (uint32_t r = 0; r < pc.rows; ++r)
+    fill_range<kWriteThrough>(a, p, pc.off + (uint64_t)r * pc.pitch, pc.row_bytes);
 }
 
 // Writer j of chunk g writes pieces [j*np/w, (j+1)*np/w) of the chunk: as
 // one byte range when the chunk is contiguous in a contiguous view (no
 // per-piece descriptor round trips), else piece by piece.
+__device__ inline bool share_is_range(const FillArgs& a, const tc::ChunkD& cd) {
+  return (cd.flags & tc::kChunkContiguous) && (a.contiguous & (1u << cd.rank));
+}
+
+template <bool kWriteThrough = false>
 __device__ void fill_share(const FillArgs& a, uint32_t g, uint32_t j) {
   const tc::ChunkD cd = a.chunks[g];
   const uint64_t lo = (uint64_t)j * cd.npieces / cd.writers;
   const uint64_t hi = (uint64_t)(j + 1) * cd.npieces / cd.writers;
   if (lo == hi) return;
-  if ((cd.flags & tc::kChunkContiguous) && (a.contiguous & (1u << cd.rank))) {
+  if (share_is_range(a, cd)) {
     const tc::PieceD first = a.pieces[cd.first_piece + lo];
     const tc::PieceD last = a.pieces[cd.first_piece + hi - 1];
-    fill_range(a, cd.rank, first.off, last.off + last.row_bytes - first.off);
+    fill_range<kWriteThrough>(a, cd.rank, first.off, last.off + last.row_bytes - first.off);
     return;
   }
-  for (uint64_t k = lo; k < hi; ++k) fill_piece(a, cd.rank, a.pieces[cd.first_piece + k]);
+  for (uint64_t k = lo; k < hi; ++k) fill_piece<kWriteThrough>(a, cd.rank, a.pieces[cd.first_piece + k]);
 }
 
 // Largest g with wprefix[g] <= slot (binary search over G + 1 entries).
@@ -202,19 +227,27 @@ __device__ inline uint32_t slot_chunk(const uint64_t* wprefix, uint32_t G, uint6
   return lo;
 }
 
-__global__ __launch_bounds__(kFillThreads) void fill_parallel_kernel(FillArgs a) {
+// One CTA per writer slot.  With kWriteThrough every store goes through to
+// memory at system scope and the mark needs no L2 write-back: a write-back
+// release flushes the whole of its XCD's L2, the other writers' dirty lines
+// included (8 ranks of one 4 MiB chunk each, 8 writers a chunk: 97 us
+// rounds against 105.5).  The buffer stores need every span under 2 GiB: a
+// share written as one byte range must be, a piece's row is by construction.
+template <bool kWriteThrough>
+__device__ void fill_parallel(const FillArgs& a) {
   const uint64_t slot = blockIdx.x;
   const uint32_t g = slot_chunk(a.wprefix, a.G, slot);
-  const uint32_t j = (uint32_t)(slot - a.wprefix[g]);
-  fill_share(a, g, j);
+  fill_share<kWriteThrough>(a, g, (uint32_t)(slot - a.wprefix[g]));
   if (a.mark == TC_MARK_INKERNEL) {
     const tc::ChunkD cd = a.chunks[g];
-    tc_mark_ready(a.h, cd.rank, cd.local);
+    if (kWriteThrough) tc_mark_ready_wt(a.h, cd.rank, cd.local);
+    else tc_mark_ready(a.h, cd.rank, cd.local);
   }
 }
 
-// One CTA per rank: its chunks in order[], each writer's share in turn, a
-// mark after each share.
+__global__ __launch_bounds__(kFillThreads) void fill_parallel_kernel(FillArgs a) { fill_parallel<false>(a); }
+__global__ __launch_bounds__(kFillThreads) void fill_parallel_wt_kernel(FillArgs a) { fill_parallel<true>(a); }
+
 __global__ __launch_bounds__(kFillThreads) void fill_serial_kernel(FillArgs a) {
   const uint32_t p = blockIdx.x;
   const uint32_t n = a.h.chunk_base[p + 1] - a.h.chunk_base[p];
@@ -395,7 +428,18 @@ int tc_produce_fill(tc_plan* P, const tc_handle* h, const tc_fill_desc* d, void*
   } else if (d->mode == TC_FILL_PARALLEL) {
     if (P->total_writers == 0) return TC_OK;
     if (P->total_writers > 0x7FFFFFFFull) return fail(TC_EINVAL, "fill: too many writers");
-    hipLaunchKernelGGL(fill_parallel_kernel, dim3((uint32_t)P->total_writers), dim3(kFillThreads), 0, s, a);
+    // Write-through when every share is one byte range under 2 GiB (every
+    // chunk one range, every view contiguous).  Shares written row by row
+    // keep plain stores: tiles' rows share cache lines, and writing them
+    // through measured slower (8 ranks of 64 x 64 u32 tiles, 4 a chunk:
+    // 108-110 us rounds against 90).
+    bool wt = P->oneshot_blocks != 0 && P->max_range_share < (1ull << 31);
+    for (uint32_t p = 0; p < P->P; ++p)
+      if (P->chunk_base[p + 1] > P->chunk_base[p] && !(a.contiguous & (1u << p))) wt = false;
+    if (wt)
+      hipLaunchKernelGGL(fill_parallel_wt_kernel, dim3((uint32_t)P->total_writers), dim3(kFillThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL(fill_parallel_kernel, dim3((uint32_t)P->total_writers), dim3(kFillThreads), 0, s, a);
   } else if (d->mode == TC_FILL_WAVES) {
     if (P->total_writers == 0) return TC_OK;
     uint32_t ctas = d->ctas;
