@@ -275,9 +275,12 @@ def run_overlap(torch, tc, workloads, seed, reps=40, cu_mask=None, engine_ctas=0
 def run_consumer_overlap(torch, tc, workloads, seed, reps=20, N2=256):
     """The 4 GEMM producers' round followed by each rank's in-kernel consumer
     (Y_q = gathered rows of replica q [8000, 2000] x W [2000, 256]), two ways:
-    consumers launched after wait() returns ("sequential"), and queued on the
-    producers' stream right behind them, waiting on the device for the
-    chunks still being copied ("chained")."""
+    consumers launched after wait() returns ("sequential"), and queued right
+    behind the producers, waiting on the device for the chunks still being
+    copied ("chained").  Chained consumers go on a stream of their own that
+    waits for an event recorded after the producers: wait() learns that the
+    producers' stream has drained as soon as the producers are done, so the
+    engine runs the completion check while the consumers wait or compute."""
     from synth import gemm_operands
     import numpy as np
     w = workloads.FULL["gemm_tiles_p4"]
@@ -298,6 +301,8 @@ def run_consumer_overlap(torch, tc, workloads, seed, reps=20, N2=256):
     Y = [torch.zeros(R * N2, dtype=torch.int16, device="cuda") for _ in range(P)]
     status = torch.zeros((P, len(start) - 1), dtype=torch.int32, device="cuda")
     prod = torch.cuda.Stream()
+    cons = torch.cuda.Stream()
+    produced = torch.cuda.Event()
 
     def producers(h):
         for p in range(P):
@@ -318,7 +323,9 @@ def run_consumer_overlap(torch, tc, workloads, seed, reps=20, N2=256):
             h = plan.start(prod)
             producers(h)
             if mode == "chained":
-                consumers(h, prod, 256)
+                produced.record(prod)
+                cons.wait_event(produced)
+                consumers(h, cons, 256)
             plan.wait(30.0)
             if mode == "sequential":
                 consumers(h, prod, 256)
