@@ -291,8 +291,13 @@ int tc_plan_start(tc_plan* plan, void* stream, tc_handle* out);
 int tc_plan_handle(const tc_plan* plan, tc_handle* out);
 
 /* Blocks until every chunk is delivered everywhere ([TP] Model: wait()):
- * waits for the copy engine and for the work queued so far on start()'s
- * stream, then runs the completion-check kernel ([TP] Gates and rounds).
+ * waits for the work queued so far on start()'s stream (the producers, so
+ * that every mark is counted) and for the copy engine, then has the
+ * completion check run ([TP] Gates and rounds): by the engine's last wave
+ * when the request reaches it soon after the last chunk is signalled, else
+ * by the check kernel.  Work queued on start()'s stream after the producers
+ * (consumers, say) delays the check until it ends: queue such work on
+ * another stream, behind an event recorded after the producers.
  *   TC_OK       STARTED -> DONE.
  *   TC_EEXTRA   a chunk got more than writers marks; state FAILED.
  *   TC_ETIMEOUT timeout_us passed; the copy engine is stopped, state stays
