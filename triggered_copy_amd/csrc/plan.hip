@@ -117,6 +117,7 @@ constexpr int kBufWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 
 constexpr int kLoadPolicy = 16;
 constexpr int kStorePolicy = 17;
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;  // offset past every buffer: access dropped
+constexpr uint32_t kQuickCountGrid = 512;      // engine grids below this many CTAs: see engine_kernel
 
 struct EngineArgs {
   uint64_t rep[TC_MAX_RANKS];
@@ -130,6 +131,7 @@ struct EngineArgs {
   uint32_t* stats;        // this launch: [0] ~first gate seen, [1] last signal (low 32 bits
                           // of the 100 MHz clock; the window is taken modulo 2^32)
   uint32_t* stop;         // this launch: set once any wave saw the abort or backstop
+  uint32_t* all_open;     // this launch: set by the publisher once every gate is open
   uint32_t* zero_launch;  // the other launch block, cleared for the next launch
   uint32_t zero_launch_words;
   uint32_t zero_round_words;
@@ -162,6 +164,16 @@ __device__ inline uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime()
 
 __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufWord3);
+}
+
+// Adds 1 to the word at p, from lane 0 only and without a lane branch: the
+// other lanes' offsets fall outside the one-word buffer and are dropped.
+// The compiler issues it and moves on.  The same count through the compiler's
+// wave-level atomic form (a scan over the lanes inside a masked branch) kept
+// the atomic's round trip, about 2.6 us here, on the path of every piece.
+__device__ inline void wave_count(uint32_t* p) {
+  (void)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, rsrc(p, 4), tc_lane_id() == 0 ? 0 : (int)kOutOfRange,
+                                                       0, 0);
 }
 
 // Whole-wave atomic add where only lane 0 contributes `v`; every lane gets
@@ -215,28 +227,23 @@ __device__ inline bool must_stop(const EngineArgs& a, uint64_t t0, uint32_t spin
 // memory system while a producer runs.  (7 and 20 us measured slower on
 // 8-rank rounds of whole chunks, 110.5 and 125-128 us p90 against 106.6: a
 // chunk waits for the last of its pieces' waves to wake.)  Other gate polls
-// ("normal") come 0.4 us apart for the first 16, then about 7 us apart: a
+// ("normal") come 0.4 us apart for the first 16, then about 3.4 us apart: a
 // short producer is caught at once, a long one (a GEMM) is not slowed by the
-// polling.  The few waves waiting on another wave of the engine (a chunk's
-// last pieces, its turn to signal) poll briskly: they are on the round's
-// critical path.  The mode must be a scalar (wave-uniform) value: see
-// gate_mode.
+// polling (7 us apart measured the same beside GEMM producers, and 2-rank
+// rounds 43 us p90 against 41).  The few waves waiting on another wave of the
+// engine (a chunk's last pieces, its turn to signal) poll briskly: they are
+// on the round's critical path.  The mode must be a scalar (wave-uniform)
+// value: see gate_mode.
 constexpr int kPollNormal = 0, kPollReserve = 1, kPollBrisk = 2;
 
 // The pause after the spins-th fruitless poll in a row.
 __device__ inline void backoff(int mode, uint32_t spins) {
-  if (spins < 8 || mode == kPollBrisk) {
+  if (spins < 8 || mode == kPollBrisk)
     __builtin_amdgcn_s_sleep(1);
-  } else if (mode == kPollNormal) {
-    if (spins < 16) {
-      __builtin_amdgcn_s_sleep(16);
-    } else {
-      __builtin_amdgcn_s_sleep(127);
-      __builtin_amdgcn_s_sleep(127);
-    }
-  } else {
+  else if (mode == kPollNormal && spins < 16)
+    __builtin_amdgcn_s_sleep(16);
+  else
     __builtin_amdgcn_s_sleep(127);
-  }
 }
 
 // Uniform spin until ready() holds.
@@ -562,6 +569,8 @@ __global__ __launch_bounds__(kEngineThreads) void engine_kernel(EngineArgs a) {
   // nothing measurable.)
   if (gw == gridDim.x * (kEngineThreads / 64) - 1) {
     const bool all = publish_gates(a, t0);
+    if (all && tc_lane_id() == 0)
+      __hip_atomic_store(a.all_open, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     if (a.chk_seq != 0) {
       if (all) engine_check(a, t0);
       else if (tc_lane_id() == 0)
@@ -576,13 +585,24 @@ __global__ __launch_bounds__(kEngineThreads) void engine_kernel(EngineArgs a) {
   // skip, the reserve sleeps (scalar instructions, which run whatever the
   // lane mask) would be taken in every mode.
   const int gate_mode = (int)tc_uniform(gridDim.x >= 256 && gw % 8 != 0 ? kPollReserve : kPollNormal);
+  // Grids under kQuickCountGrid CTAs count pieces with wave_count once the
+  // publisher has seen every gate open (checked with each ticket until then).
+  // Counted that way from the start, the copies beside 4 GEMM producers ran
+  // faster while the producers ran and slowed them by 8-9% (against 6%); at
+  // 1024 CTAs it cost the all-gather 0.5 points of HBM peak.  Switched on once
+  // every gate is open: GEMM rounds 126 us against 135 at the same slowdown,
+  // 2-rank rounds 37-39 us against 42, 8-rank rounds 97 against 99.
+  const bool small_grid = gridDim.x < kQuickCountGrid;
+  bool quick = false;
 
   for (uint32_t s = 0; s < a.nranks; ++s) {
     const uint32_t p = (gw + s) % a.nranks;
     const uint32_t np = a.piece_base[p + 1] - a.piece_base[p];
     if (np == 0) continue;
     for (;;) {
+      const uint32_t opened = small_grid && !quick ? wave_load(a.all_open) : 0u;
       const uint32_t t = wave_add(a.tickets + p * kTicketStride, 1u);
+      if (opened != 0) quick = true;
       if (t >= np) break;
       const PieceD pc = a.pieces[a.piece_base[p] + t];
       const uint32_t g = tc_uniform(pc.chunk);
@@ -618,7 +638,10 @@ __global__ __launch_bounds__(kEngineThreads) void engine_kernel(EngineArgs a) {
       // chunk is visible, which lets an earlier chunk's signaller take it).
       const ChunkD cd = a.chunks[g];
       uint32_t* done = a.done + (uint64_t)g * kTicketStride;
-      wave_add_noret(done, 1u);
+      if (quick)
+        wave_count(done);
+      else
+        wave_add_noret(done, 1u);
       if (a.piece_base[p] + t + 1 != cd.first_piece + cd.npieces) continue;
       if (!poll_until(a, t0, kPollBrisk, [&] { return wave_load(done) >= cd.npieces; })) return;
       if (!signal_in_order(a, p, cd.local, g, t0)) return;
@@ -729,6 +752,7 @@ static int launch_engine(tc_plan* P) {
   a.tickets = reinterpret_cast<uint32_t*>(cur_launch);
   a.stats = reinterpret_cast<uint32_t*>(cur_launch + (uint64_t)P->P * kTicketStride * 4);
   a.stop = reinterpret_cast<uint32_t*>(cur_launch + (uint64_t)P->P * kTicketStride * 4 + kStatsWords * 8);
+  a.all_open = a.stop + 16;  // the stop word's line, 64 bytes in
   a.done = reinterpret_cast<uint32_t*>(cur_launch + (uint64_t)P->P * kTicketStride * 4 + kStatsWords * 8 + 128);
   a.zero_launch = reinterpret_cast<uint32_t*>(P->ws + L.launch[lb ^ 1u]);
   a.zero_launch_words = (uint32_t)(L.launch_bytes / 4);
