@@ -215,7 +215,7 @@ typedef struct tc_plan_desc {
   const uint32_t* cu_mask;             /* NULL = copy engine may use every CU */
   uint32_t cu_mask_words;
   uint32_t engine_ctas;                /* CTAs of 4 waves (the grid's last wave publishes the
-                                          gates, the others copy); 0 = one wave per 192 KiB of
+                                          gates, the others copy); 0 = one wave per 150 KiB of
                                           delivered bytes per round (source bytes times the
                                           P - 1 receivers), at least one per piece up to 256
                                           plus the publisher, at most 16 waves per usable CU */

@@ -1269,11 +1269,15 @@ static int create_plan(const tc_plan_desc* d, uint8_t* ws, uint64_t ws_bytes,
 
   // Default engine size: one worker wave per piece up to 256 (small rounds
   // are latency-bound: every piece in flight at once), otherwise one wave per
-  // 192 KiB of delivered bytes per round, at most 16 per usable CU (the count
+  // 150 KiB of delivered bytes per round, at most 16 per usable CU (the count
   // that saturates HBM).  A wave's work is what it writes: each piece it
   // reads goes to all P - 1 receivers.  Fewer waves leave the producer's CUs
-  // quieter when a round moves little data.  One more wave is the gate
-  // publisher, which copies nothing.
+  // quieter when a round moves little data; more copy a finished producer's
+  // chunks sooner.  (Beside 4 GEMM producers delivering 96 MB a round: one
+  // wave per 192 KiB, 122 CTAs, gave 127 us rounds at 3.8-4.0% producer
+  // slowdown; per 150 KiB, 157 CTAs, 118-119 us at 4.1-5.6%; per 128 KiB,
+  // 183 CTAs, 115.5 us at 4.9-5.2%.)  One more wave is the gate publisher,
+  // which copies nothing.
   const uint32_t npieces = (uint32_t)P->pieces.size();
   uint64_t src_bytes = 0;
   for (const ChunkD& c : P->chunks) src_bytes += c.bytes;
@@ -1283,7 +1287,7 @@ static int create_plan(const tc_plan_desc* d, uint8_t* ws, uint64_t ws_bytes,
   } else {
     const uint64_t waves = std::min<uint64_t>(
         16ull * usable,
-        std::max<uint64_t>(std::min<uint64_t>(npieces, 256) + 1, delivered / (192u << 10)));
+        std::max<uint64_t>(std::min<uint64_t>(npieces, 256) + 1, delivered / (150u << 10)));
     P->engine_ctas = (uint32_t)((waves + 3) / 4);
   }
   P->engine_ctas = std::max<uint32_t>(
