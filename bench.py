@@ -726,12 +726,14 @@ def main():
                                              cu_mask=overlap_mask(torch, args.overlap_cus),
                                              engine_ctas=args.overlap_engine_ctas)
         extras["gemm_overlap"]["engine_cus"] = args.overlap_cus or "all"
-        # The same rounds with a larger engine (160 CTAs): a shorter round for
-        # about the same producer slowdown.
-        log("overlap: the same with 160 engine CTAs")
-        extras["gemm_overlap_160"] = run_overlap(torch, tc, workloads, BASE_SEED,
+        # The same rounds with a smaller engine (122 CTAs, one wave per 192 KiB
+        # delivered): less copying beside the producers, a longer round.
+        log("overlap: the same with 122 engine CTAs")
+        extras["gemm_overlap_122"] = run_overlap(torch, tc, workloads, BASE_SEED,
                                                  cu_mask=overlap_mask(torch, args.overlap_cus),
-                                                 engine_ctas=160)
+                                                 engine_ctas=122)
+        log("GEMM producers alone, device-timed, and the library GEMM")
+        extras["gemm_only"] = run_gemm_only(torch, tc, workloads, BASE_SEED, 100)
         log("in-kernel consumers: after wait() vs waiting on the device")
         extras["gemm_consumer"] = run_consumer_overlap(torch, tc, workloads, BASE_SEED)
         log("barrier: 8 ranks x 1000 generations")
