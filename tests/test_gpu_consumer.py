@@ -78,10 +78,14 @@ def test_consumer_waits_for_filled_tiles():
         pair.close()
 
 
-def test_consumer_of_gemm_producers():
+@pytest.mark.parametrize("consumer_stream", ["producers", "own"])
+def test_consumer_of_gemm_producers(consumer_stream):
     # The 4-rank GEMM producer workload; each rank's consumer multiplies the
     # gathered [8000, 2000] rows by a [2000, 256] weight while the producers
-    # and the copy engine still run.
+    # and the copy engine still run.  The consumers go on the producers'
+    # stream, or on a stream of their own behind an event recorded after the
+    # producers (so that wait() sees the producers' stream drain as soon as
+    # the producers end).
     w = workloads.FULL["gemm_tiles_p4"]
     P, M, N, K = w["P"], w["rows"], w["cols"], w["K"]
     pair = Pair(w, oracle_bytes=False)
@@ -105,9 +109,16 @@ def test_consumer_of_gemm_producers():
             tc.gemm_bf16(ops[p][0], ops[p][1], pair.rep[p][p * M * N * 2:], ldc=N, M=M, N=N,
                          programs=w["programs"], group_m=w["group_m"], handle=h, rank=p,
                          first_chunk=0, tiles_per_chunk=w["tiles_per_chunk"], stream=pair.stream)
+        cons = pair.stream
+        if consumer_stream == "own":
+            cons = torch.cuda.Stream()
+            produced = torch.cuda.Event()
+            produced.record(pair.stream)
+            cons.wait_event(produced)
+        log(f"GEMM producers, consumers on the {consumer_stream} stream")
         for q in range(P):
             tc.gemm_consume_bf16(h, q, ds, dp, pair.rep[q], wt, Y[q], M=R, N=N2, K=N,
-                                 status=status[q], programs=256, stream=pair.stream)
+                                 status=status[q], programs=256, stream=cons)
         pair.plan.wait(30.0)
         torch.cuda.synchronize()
         # The gathered rows: each rank's own block as its producer wrote it.
