@@ -101,19 +101,24 @@ ONESHOT_CASES = {
 }
 
 
+@pytest.mark.parametrize("fill", ["oneshot", "writer_ctas"])
 @pytest.mark.parametrize("name", sorted(ONESHOT_CASES))
-def test_oneshot_fill(name):
-    # One CTA per 16 KiB block of each writer's share; the share's last
-    # block to finish marks.  Rounds alternate in-kernel and deferred marks,
-    # so a deferred round must leave the block counters as it found them.
+def test_range_share_fills(name, fill):
+    # Every chunk one byte range in a contiguous view.  oneshot: one CTA per
+    # 16 KiB block of each writer's share, the share's last block to finish
+    # marks.  writer_ctas: one CTA per writer, which then writes its share
+    # through to memory and marks without an L2 write-back.  Shares that
+    # start and end off 16-byte boundaries take the byte path.  Rounds
+    # alternate in-kernel and deferred marks, so a deferred round must leave
+    # the block counters as it found them.
     w = ONESHOT_CASES[name]
     pair = Pair(w, piece_bytes=4096)
     try:
         for r, mark in ((1, True), (2, False), (3, True), (4, True)):
-            log(f"oneshot {name} round {r} mark={mark}")
-            pair.gpu_round_fill(mark=mark, oneshot=True)
+            log(f"{fill} {name} round {r} mark={mark}")
+            pair.gpu_round_fill(mark=mark, oneshot=fill == "oneshot")
             pair.oracle_round()
-            pair.compare(f"oneshot {name} round {r}")
+            pair.compare(f"{fill} {name} round {r}")
             pair.plan.next_round()
             pair.sim.next_round()
     finally:
@@ -467,12 +472,13 @@ def test_random_hand_built_tables(case):
 
 
 @pytest.mark.parametrize("case", range(16))
-def test_random_byte_range_tables_oneshot_fill(case):
+def test_random_byte_range_tables_range_fills(case):
     # Every rank's bytes cut at random points into linear regions, grouped
     # into chunks of 1-3 adjacent regions with 1-6 writers (more writers
     # than pieces leaves empty shares), random piece sizes: the one-shot
-    # fill's share and block tables against the oracle over 3 rounds, the
-    # second with deferred marks.
+    # fill's share and block tables (even cases) or the write-through writer
+    # CTAs (odd cases) against the oracle over 3 rounds, the second with
+    # deferred marks.
     from oracle import schedule as osched
     rng = np.random.default_rng(3000 + case)
     P = int(rng.integers(2, 6))
@@ -498,7 +504,7 @@ def test_random_byte_range_tables_oneshot_fill(case):
                   engine_ctas=int(rng.integers(1, 9)))
         log(f"random byte-range tables case {case}: P={P} bytes/rank={n} {kw}")
         _swap_in(pair, ts, os_, **kw)
-        _rounds(pair, 3, f"random byte ranges case {case}", deferred=(2,), oneshot=True)
+        _rounds(pair, 3, f"random byte ranges case {case}", deferred=(2,), oneshot=case % 2 == 0)
     finally:
         pair.close()
 
