@@ -27,6 +27,9 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kFillThreads = 256;
+// One-shot blocks: 16 KiB each, 128 threads (8 vectors a thread): 5.62-5.65 ms per
+// all-gather step against 5.67-5.68 with 256 threads, 6.17-6.20 with 512.
+constexpr int kOneShotThreads = 128;
 
 __host__ __device__ inline uint64_t mix64(uint64_t z) {
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
@@ -110,8 +113,9 @@ __device__ inline void put_byte(uint8_t* d, __amdgpu_buffer_rsrc_t wt, uint32_t 
 // index of byte `off`.  With kWriteThrough the stores go through to memory
 // at system scope (len < 2^31), so that once they complete the bytes are
 // visible to every CU without an L2 write-back.  kIlp 4 computes four vectors
-// per thread before storing them (for long spans), 1 one at a time.
-template <bool kWriteThrough, int kIlp = 4>
+// per thread before storing them (for long spans), 1 one at a time; kThreads
+// is the CTA's thread count.
+template <bool kWriteThrough, int kIlp = 4, int kThreads = kFillThreads>
 __device__ void fill_span(const FillArgs& a, uint32_t p, uint64_t off, uint64_t len, uint64_t idx0) {
   uint8_t* base = reinterpret_cast<uint8_t*>(a.rep[p]);
   const __amdgpu_buffer_rsrc_t wt =
@@ -154,25 +158,25 @@ __device__ void fill_span(const FillArgs& a, uint32_t p, uint64_t off, uint64_t 
     // so one wave per SIMD keeps the arithmetic units busy (a CTA of more
     // waves might not fit beside a persistent copy engine that fills the
     // CU's other slots, and must run while it waits for the marks).  A
-    // 16 KiB one-shot block (four vectors per thread in all) stores each
-    // vector as soon as it is computed: 5.672 ms per headline step against
-    // 5.697 with the four computed first.
+    // 16 KiB one-shot block stores each vector as soon as it is computed
+    // (with 256 threads, four vectors each: 5.672 ms per all-gather step
+    // against 5.697 with the four computed first).
     uint64_t v = threadIdx.x;
     if (kIlp == 4) {
-      for (; v + 3 * kFillThreads < nv; v += 4 * kFillThreads) {
-        const u32x4 o0 = value(v), o1 = value(v + kFillThreads), o2 = value(v + 2 * kFillThreads),
-                    o3 = value(v + 3 * kFillThreads);
+      for (; v + 3 * kThreads < nv; v += 4 * kThreads) {
+        const u32x4 o0 = value(v), o1 = value(v + kThreads), o2 = value(v + 2 * kThreads),
+                    o3 = value(v + 3 * kThreads);
         put(v, o0);
-        put(v + kFillThreads, o1);
-        put(v + 2 * kFillThreads, o2);
-        put(v + 3 * kFillThreads, o3);
+        put(v + kThreads, o1);
+        put(v + 2 * kThreads, o2);
+        put(v + 3 * kThreads, o3);
       }
     }
-    for (; v < nv; v += kFillThreads) put(v, value(v));
+    for (; v < nv; v += kThreads) put(v, value(v));
   } else {
     const uint64_t n = len / e;
     uint8_t* d = base + off;
-    for (uint64_t i = threadIdx.x; i < n; i += kFillThreads) {
+    for (uint64_t i = threadIdx.x; i < n; i += kThreads) {
       const uint64_t h = key_hash(kh, (uint32_t)(idx0 + i));
       const uint32_t at = (uint32_t)(i * e);
       if (a.kind == TC_FILL_U32) {
@@ -296,7 +300,7 @@ __global__ __launch_bounds__(kFillThreads) void fill_waves_kernel(FillArgs a) {
 // block that completes the count issues the writer's mark, so each writer
 // slot still marks its chunk exactly once per round.  Counting happens only
 // when the fill marks: a deferred-mark fill leaves the counters at zero.
-__global__ __launch_bounds__(kFillThreads) void fill_oneshot_kernel(FillArgs a) {
+__global__ __launch_bounds__(kOneShotThreads) void fill_oneshot_kernel(FillArgs a) {
   const uint64_t b = blockIdx.x;
   uint64_t lo = 0, hi = a.nshares;  // largest s with shares[s].first_block <= b
   while (hi - lo > 1) {
@@ -311,7 +315,7 @@ __global__ __launch_bounds__(kFillThreads) void fill_oneshot_kernel(FillArgs a) 
     const uint32_t p = a.chunks[sh.g].rank;
     const uint64_t rel = sh.off + at - a.view_off[p];
     const uint64_t idx0 = a.elem == 4 ? rel >> 2 : a.elem == 2 ? rel >> 1 : rel;
-    fill_span<true, 1>(a, p, sh.off + at, min(tc::kOneShotBlock, sh.bytes - at), idx0);
+    fill_span<true, 1, kOneShotThreads>(a, p, sh.off + at, min(tc::kOneShotBlock, sh.bytes - at), idx0);
   }
   if (a.mark != TC_MARK_INKERNEL) return;
   __shared__ uint32_t last;
@@ -467,7 +471,7 @@ int tc_produce_fill(tc_plan* P, const tc_handle* h, const tc_fill_desc* d, void*
     a.shares = reinterpret_cast<const tc::ShareD*>(P->ws + P->L.shares);
     a.share_ctr = reinterpret_cast<uint64_t*>(P->ws + P->L.share_ctr);
     a.nshares = P->total_writers;
-    hipLaunchKernelGGL(fill_oneshot_kernel, dim3((uint32_t)P->oneshot_blocks), dim3(kFillThreads), 0, s, a);
+    hipLaunchKernelGGL(fill_oneshot_kernel, dim3((uint32_t)P->oneshot_blocks), dim3(kOneShotThreads), 0, s, a);
   } else {
     return fail(TC_EINVAL, "fill: unknown mode");
   }
