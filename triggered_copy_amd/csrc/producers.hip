@@ -275,8 +275,11 @@ __global__ __launch_bounds__(kFillThreads) void fill_serial_kernel(FillArgs a) {
 
 // Persistent grid: writer slots in waves (every rank's chunk 0 writers,
 // then every rank's chunk 1 writers, ...); CTA i takes slots i, i + ctas, ...
-// All loop bounds and indices are uniform over the CTA.
-__global__ __launch_bounds__(kFillThreads) void fill_waves_kernel(FillArgs a) {
+// All loop bounds and indices are uniform over the CTA.  kWriteThrough as in
+// fill_parallel (fully triggered rounds of 4 x 1.5 GiB: 5.80-5.85 ms against
+// 5.84-5.88 with write-back stores and marks).
+template <bool kWriteThrough>
+__device__ void fill_waves(const FillArgs& a) {
   uint64_t slot = 0;
   for (uint32_t c = 0; c < a.max_chunks; ++c) {
     for (uint32_t p = 0; p < a.h.nranks; ++p) {
@@ -286,13 +289,19 @@ __global__ __launch_bounds__(kFillThreads) void fill_waves_kernel(FillArgs a) {
       // This CTA's slots among [slot, slot + w): j = first, first + grid, ...
       const uint64_t first = (blockIdx.x + gridDim.x - slot % gridDim.x) % gridDim.x;
       for (uint64_t j = first; j < w; j += gridDim.x) {
-        fill_share(a, g, (uint32_t)j);
-        if (a.mark == TC_MARK_INKERNEL) tc_mark_ready(a.h, p, c);
+        fill_share<kWriteThrough>(a, g, (uint32_t)j);
+        if (a.mark == TC_MARK_INKERNEL) {
+          if (kWriteThrough) tc_mark_ready_wt(a.h, p, c);
+          else tc_mark_ready(a.h, p, c);
+        }
       }
       slot += w;
     }
   }
 }
+
+__global__ __launch_bounds__(kFillThreads) void fill_waves_kernel(FillArgs a) { fill_waves<false>(a); }
+__global__ __launch_bounds__(kFillThreads) void fill_waves_wt_kernel(FillArgs a) { fill_waves<true>(a); }
 
 // One-shot grid: CTA b writes block b of the share table (kOneShotBlock
 // bytes of one writer's share of a contiguous chunk) with write-through
@@ -391,6 +400,19 @@ __global__ __launch_bounds__(256) void consume_kernel(ConsumeArgs a) {
 
 extern "C" {
 
+// Whether the writer-CTA fills (parallel and waves) store write-through and
+// mark without an L2 write-back: when every share is one byte range under
+// 2 GiB (every chunk one range, every view contiguous).  Shares written row
+// by row keep plain stores: tiles' rows share cache lines, and writing them
+// through measured slower (8 ranks of 64 x 64 u32 tiles, 4 a chunk: 108-110
+// us rounds against 90).
+static bool shares_write_through(const tc_plan* P, const FillArgs& a) {
+  if (P->oneshot_blocks == 0 || P->max_range_share >= (1ull << 31)) return false;
+  for (uint32_t p = 0; p < P->P; ++p)
+    if (P->chunk_base[p + 1] > P->chunk_base[p] && !(a.contiguous & (1u << p))) return false;
+  return true;
+}
+
 int tc_produce_fill(tc_plan* P, const tc_handle* h, const tc_fill_desc* d, void* stream) {
   if (!P || !h || !d || !d->views) return fail(TC_EINVAL, "fill: NULL argument");
   const uint32_t elem = d->kind == TC_FILL_U32 ? 4 : d->kind == TC_FILL_BF16 ? 2 : d->kind == TC_FILL_U8 ? 1 : 0;
@@ -438,15 +460,7 @@ int tc_produce_fill(tc_plan* P, const tc_handle* h, const tc_fill_desc* d, void*
   } else if (d->mode == TC_FILL_PARALLEL) {
     if (P->total_writers == 0) return TC_OK;
     if (P->total_writers > 0x7FFFFFFFull) return fail(TC_EINVAL, "fill: too many writers");
-    // Write-through when every share is one byte range under 2 GiB (every
-    // chunk one range, every view contiguous).  Shares written row by row
-    // keep plain stores: tiles' rows share cache lines, and writing them
-    // through measured slower (8 ranks of 64 x 64 u32 tiles, 4 a chunk:
-    // 108-110 us rounds against 90).
-    bool wt = P->oneshot_blocks != 0 && P->max_range_share < (1ull << 31);
-    for (uint32_t p = 0; p < P->P; ++p)
-      if (P->chunk_base[p + 1] > P->chunk_base[p] && !(a.contiguous & (1u << p))) wt = false;
-    if (wt)
+    if (shares_write_through(P, a))
       hipLaunchKernelGGL(fill_parallel_wt_kernel, dim3((uint32_t)P->total_writers), dim3(kFillThreads), 0, s, a);
     else
       hipLaunchKernelGGL(fill_parallel_kernel, dim3((uint32_t)P->total_writers), dim3(kFillThreads), 0, s, a);
@@ -460,7 +474,10 @@ int tc_produce_fill(tc_plan* P, const tc_handle* h, const tc_fill_desc* d, void*
     }
     for (uint32_t p = 0; p < P->P; ++p)
       a.max_chunks = std::max(a.max_chunks, P->chunk_base[p + 1] - P->chunk_base[p]);
-    hipLaunchKernelGGL(fill_waves_kernel, dim3(ctas), dim3(kFillThreads), 0, s, a);
+    if (shares_write_through(P, a))
+      hipLaunchKernelGGL(fill_waves_wt_kernel, dim3(ctas), dim3(kFillThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL(fill_waves_kernel, dim3(ctas), dim3(kFillThreads), 0, s, a);
   } else if (d->mode == TC_FILL_ONESHOT) {
     if (P->total_writers == 0) return TC_OK;
     if (P->oneshot_blocks == 0) return fail(TC_EINVAL, "fill: one-shot mode needs every chunk to be one byte range");
