@@ -171,14 +171,17 @@ def run_headline(args, torch, tc, workloads, seed):
     # Full triggered rounds: the fill marks each chunk as its writers finish,
     # so copies overlap the production of later chunks.  The producer is the
     # persistent writer grid (every rank's chunk 0 first, then chunk 1, ...):
-    # with the engine running beside it, it beats the one-shot grid.
+    # with the engine running beside it, it beats the one-shot grid.  Beside
+    # the engine, 3 CTAs per CU (5.77-5.80 ms rounds) beat the fill's own
+    # default of 2 (5.83-5.86), which is best for the fill alone.
     if not args.no_extras:
         times = []
+        wave_ctas = 3 * torch.cuda.get_device_properties(0).multi_processor_count
         for i in range(max(3, args.steps // 4)):
             torch.cuda.synchronize()
             a = time.perf_counter()
             h = plan.start(prod)
-            plan.fill(h, views, seed, kind=w["elem"], mark=True, waves=True, stream=prod)
+            plan.fill(h, views, seed, kind=w["elem"], mark=True, waves=True, ctas=wave_ctas, stream=prod)
             plan.wait(60.0)
             plan.next_round()
             times.append(time.perf_counter() - a)
