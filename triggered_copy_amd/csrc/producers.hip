@@ -98,6 +98,13 @@ __device__ inline uint64_t index_at(const FillArgs& a, uint32_t p, uint64_t off)
   return r * a.view_cols[p] + (rel - r * a.view_pitch[p]) / a.elem;
 }
 
+// The fill is a producer: its waves take the highest issue priority over
+// the copy engine's waves sharing their SIMDs (the engine waits for what the
+// producer writes).  Fully triggered 4 x 1.5 GiB rounds (waves fill, 3 CTAs
+// per CU): 5.67-5.71 ms against 5.75-5.79 without it; the small rounds and
+// the deferred-mark all-gather are unchanged or slightly faster.
+__device__ inline void producer_priority() { __builtin_amdgcn_s_setprio(3); }
+
 // Byte `at` of a range starting at d: a plain store, or a write-through
 // buffer store through `wt` (the same range's descriptor).
 template <bool kWriteThrough>
@@ -245,6 +252,7 @@ __device__ inline uint32_t slot_chunk(const uint64_t* wprefix, uint32_t G, uint6
 // share written as one byte range must be, a piece's row is by construction.
 template <bool kWriteThrough>
 __device__ void fill_parallel(const FillArgs& a) {
+  producer_priority();
   const uint64_t slot = blockIdx.x;
   const uint32_t g = slot_chunk(a.wprefix, a.G, slot);
   fill_share<kWriteThrough>(a, g, (uint32_t)(slot - a.wprefix[g]));
@@ -259,6 +267,7 @@ __global__ __launch_bounds__(kFillThreads) void fill_parallel_kernel(FillArgs a)
 __global__ __launch_bounds__(kFillThreads) void fill_parallel_wt_kernel(FillArgs a) { fill_parallel<true>(a); }
 
 __global__ __launch_bounds__(kFillThreads) void fill_serial_kernel(FillArgs a) {
+  producer_priority();
   const uint32_t p = blockIdx.x;
   const uint32_t n = a.h.chunk_base[p + 1] - a.h.chunk_base[p];
   for (uint32_t k = 0; k < n; ++k) {
@@ -280,6 +289,7 @@ __global__ __launch_bounds__(kFillThreads) void fill_serial_kernel(FillArgs a) {
 // 5.84-5.88 with write-back stores and marks).
 template <bool kWriteThrough>
 __device__ void fill_waves(const FillArgs& a) {
+  producer_priority();
   uint64_t slot = 0;
   for (uint32_t c = 0; c < a.max_chunks; ++c) {
     for (uint32_t p = 0; p < a.h.nranks; ++p) {
@@ -310,6 +320,7 @@ __global__ __launch_bounds__(kFillThreads) void fill_waves_wt_kernel(FillArgs a)
 // slot still marks its chunk exactly once per round.  Counting happens only
 // when the fill marks: a deferred-mark fill leaves the counters at zero.
 __global__ __launch_bounds__(kOneShotThreads) void fill_oneshot_kernel(FillArgs a) {
+  producer_priority();
   const uint64_t b = blockIdx.x;
   uint64_t lo = 0, hi = a.nshares;  // largest s with shares[s].first_block <= b
   while (hi - lo > 1) {
