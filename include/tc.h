@@ -378,7 +378,8 @@ typedef struct tc_stats {
   uint64_t bytes_read;     /* bytes the engine reads per round (each chunk once) */
   uint64_t pieces;         /* copy work units per round */
   uint32_t G;              /* total chunks */
-  uint32_t rsvd;
+  uint32_t engine_checked; /* 1: the last wait()'s completion check ran inside the copy
+                              engine; 0: the check kernel ran it */
 } tc_stats;
 
 int tc_plan_stats(tc_plan* plan, tc_stats* out);

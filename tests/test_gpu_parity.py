@@ -669,6 +669,55 @@ def test_extra_mark_fails_the_plan():
         pair.close()
 
 
+# (P, chunks per rank): by gate rows over several passes and two batches of
+# 64 (2, 40), over three passes (8, 3); one lane per chunk over two batches
+# (3, 30) and (16, 5).
+@pytest.mark.parametrize("P,n", [(2, 40), (8, 3), (3, 30), (16, 5)])
+def test_in_engine_check_names_the_chunks_the_oracle_names(P, n):
+    # The copy engine's own completion check covers the chunks either one
+    # gate row per lane or one chunk per lane, batch by batch of up to 64,
+    # and must name exactly the chunks the oracle names in any of them.  The
+    # engine runs the check only if wait()'s request reaches it within its
+    # polling window (else the check kernel runs it, with the same result),
+    # so a fresh plan is tried again, a few times at most, until the engine
+    # did.
+    w = dict(P=P, rows=4 * n, cols=64, elem="u32", builder="chunks", n=n, writers=1, rounds=2)
+    extra = [(0, 1), (P // 2, n - 2), (P - 1, n - 1)]
+    paths = []
+    for attempt in range(4):
+        pair = Pair(w)
+        try:
+            assert pair.plan.G == P * n
+            log(f"in-engine check P={P} n={n} attempt {attempt} round 1")
+            h = pair.plan.start(pair.stream)
+            pair.plan.fill(h, pair.tv, pair.seed, kind="u32", stream=pair.stream)
+            pair.plan.wait(10.0)
+            paths.append(pair.plan.stats()["engine_checked"])
+            pair.oracle_round()
+            pair.compare(f"in-engine check P={P} round 1")
+            pair.plan.next_round()
+            pair.sim.next_round()
+            log(f"in-engine check P={P} n={n} attempt {attempt} round 2")
+            h = pair.plan.start(pair.stream)
+            pair.plan.fill(h, pair.tv, pair.seed, kind="u32", stream=pair.stream)
+            for p, c in extra:
+                pair.plan.mark(h, p, c, 1, stream=pair.stream)
+            with pytest.raises(tc.ExtraMarksError) as ei:
+                pair.plan.wait(10.0)
+            in_engine = pair.plan.stats()["engine_checked"]
+            paths.append(in_engine)
+            with pytest.raises(oplan.PlanError) as eo:
+                pair.oracle_round(extra=extra)
+            assert eo.value.code == "EEXTRA"
+            assert sorted(ei.value.chunks) == sorted(eo.value.chunks) == sorted(extra)
+        finally:
+            pair.close()
+        if in_engine:
+            break
+    log(f"check paths (1 = in the engine): {paths}")
+    assert paths[-1] == 1
+
+
 def test_state_order_and_round_limit():
     w = dict(P=2, rows=4, cols=64, elem="u32", builder="whole", writers=1, rounds=1)
     pair = Pair(w)

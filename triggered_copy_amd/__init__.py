@@ -420,7 +420,7 @@ class TriggeredPlan:
     def stats(self) -> dict:
         s = _lib.Stats()
         _check(lib().tc_plan_stats(self._p, C.byref(s)))
-        return {k: getattr(s, k) for k, _ in s._fields_ if k != "rsvd"}
+        return {k: getattr(s, k) for k, _ in s._fields_}
 
     def engine_stream(self) -> int:
         out = C.c_void_p()

@@ -50,7 +50,7 @@ class PlanDesc(C.Structure):
 class Stats(C.Structure):
     _fields_ = [("engine_ms", C.c_float), ("launches", u32), ("engine_ctas", u32),
                 ("window_ticks", u64), ("bytes_moved", u64), ("bytes_read", u64),
-                ("pieces", u64), ("G", u32), ("rsvd", u32)]
+                ("pieces", u64), ("G", u32), ("engine_checked", u32)]
 
 
 class FillDesc(C.Structure):

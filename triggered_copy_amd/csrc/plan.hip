@@ -400,38 +400,57 @@ __device__ inline uint64_t ld(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// Flags of global chunk g: its counters against what a complete round r
-// leaves ([TP] Gates and rounds: this rank's chunk marked by all its writers
-// and arrived at every peer).  Per lane.
+// A chunk's counters against what a complete round r leaves ([TP] Gates and
+// rounds: this rank's chunk marked by all its writers and arrived at every
+// peer).  Every word is loaded before any is judged, and the judging has no
+// branch, so that one wait covers all the loads of a lane.
+
+// One gate row (rank q's row of chunk g), as loaded.
+struct RowWords {
+  uint64_t ready, arrival, other;  // other: writers | rsvd[0..4], all zero
+};
+
+__device__ inline RowWords load_row(const CheckView& a, uint32_t g, uint32_t q) {
+  const tc_gate_row* r = reinterpret_cast<const tc_gate_row*>(
+      a.gates + (uint64_t)q * a.gate_stride + (uint64_t)g * TC_GATE_ROW_BYTES);
+  uint64_t w[5];
+  for (int k = 0; k < 5; ++k) w[k] = ld(&r->rsvd[k]);
+  const uint64_t wr = ld(&r->writers), arr = ld(&r->arrival), rdy = ld(&r->ready);
+  return RowWords{rdy, arr, wr | w[0] | w[1] | w[2] | w[3] | w[4]};
+}
+
+// Rank q's row is the sender's own when own: no arrival there, and `ready`
+// is this round once the gate has opened (it is stored before the chunk is
+// signalled anywhere).  Every other row holds an arrival and no `ready`.
+__device__ inline uint32_t judge_row(const RowWords& w, bool own, uint32_t round) {
+  const uint32_t f_own = ((w.arrival != 0 || w.ready > round) ? kFlagCorrupt : 0u) |
+                         (w.ready < round ? kFlagNotArrived : 0u);
+  const uint32_t f_peer = ((w.ready != 0 || w.arrival > round) ? kFlagCorrupt : 0u) |
+                          (w.arrival < round ? kFlagNotArrived : 0u);
+  return (w.other != 0 ? kFlagCorrupt : 0u) | (own ? f_own : f_peer);
+}
+
+// The sum of chunk g's mark stripes.
+__device__ inline uint64_t load_marks(const CheckView& a, uint32_t g) {
+  uint64_t m[TC_MARK_STRIPES];
+  for (uint32_t k = 0; k < TC_MARK_STRIPES; ++k)
+    m[k] = ld(reinterpret_cast<const uint64_t*>(
+        a.marks + ((uint64_t)g * TC_MARK_STRIPES + k) * TC_MARK_STRIPE_BYTES));
+  uint64_t sum = 0;
+  for (uint32_t k = 0; k < TC_MARK_STRIPES; ++k) sum += m[k];
+  return sum;
+}
+
+__device__ inline uint32_t judge_marks(uint64_t marks, uint32_t writers, uint32_t round) {
+  const uint64_t want = (uint64_t)round * writers;
+  return (marks > want ? kFlagExtra : 0u) | (marks < want ? kFlagShortMarks : 0u);
+}
+
+// Every flag of chunk g, one lane alone (the check kernel's way).
 __device__ uint32_t check_chunk(const CheckView& a, uint32_t g) {
   const ChunkD cd = a.chunks[g];
-  const uint64_t want = (uint64_t)a.round * cd.writers;
-  uint64_t marks = 0;
-  for (uint32_t k = 0; k < TC_MARK_STRIPES; ++k)
-    marks += ld(reinterpret_cast<const uint64_t*>(
-        a.marks + ((uint64_t)g * TC_MARK_STRIPES + k) * TC_MARK_STRIPE_BYTES));
-  uint32_t f = 0;
-  if (marks > want) f |= kFlagExtra;
-  if (marks < want) f |= kFlagShortMarks;
-  for (uint32_t q = 0; q < a.nranks; ++q) {
-    const tc_gate_row* r = reinterpret_cast<const tc_gate_row*>(
-        a.gates + (uint64_t)q * a.gate_stride + (uint64_t)g * TC_GATE_ROW_BYTES);
-    for (int k = 0; k < 5; ++k)
-      if (ld(&r->rsvd[k]) != 0) f |= kFlagCorrupt;
-    if (ld(&r->writers) != 0) f |= kFlagCorrupt;
-    const uint64_t arr = ld(&r->arrival);
-    const uint64_t rdy = ld(&r->ready);
-    if (q == cd.rank) {
-      // The sender's row: no arrival; `ready` is this round once the gate
-      // has opened (it is stored before the chunk is signalled anywhere).
-      if (arr != 0 || rdy > a.round) f |= kFlagCorrupt;
-      if (rdy < a.round) f |= kFlagNotArrived;
-      continue;
-    }
-    if (rdy != 0) f |= kFlagCorrupt;
-    if (arr < a.round) f |= kFlagNotArrived;
-    if (arr > a.round) f |= kFlagCorrupt;
-  }
+  uint32_t f = judge_marks(load_marks(a, g), cd.writers, a.round);
+  for (uint32_t q = 0; q < a.nranks; ++q) f |= judge_row(load_row(a, g, q), q == cd.rank, a.round);
   return f;
 }
 
@@ -446,7 +465,7 @@ struct CheckArgs {
 
 constexpr int kCheckThreads = 1024;
 // Plans of up to this many chunks have their completion check run by the
-// engine's publisher (one wave, 64 chunks at a time); larger ones by the
+// engine's publisher (one wave, 64 / P chunks at a time); larger ones by the
 // check kernel.
 constexpr uint32_t kEngineCheckMaxChunks = 256;
 
@@ -506,7 +525,7 @@ __device__ bool publish_gates(const EngineArgs& a, uint64_t t0) {
 // flags as the check kernel's, the engine status handed over, then the
 // sequence word.  Otherwise -- no request within kRequestPolls polls, or the
 // launch must stop -- it reports leaving unchecked through chk_exit, and the
-// host runs the check kernel instead.  Whole wave; chunks in lanes.
+// host runs the check kernel instead.  Whole wave.
 constexpr uint32_t kRequestPolls = 48;
 
 __device__ void engine_check(const EngineArgs& a, uint64_t t0) {
@@ -527,15 +546,56 @@ __device__ void engine_check(const EngineArgs& a, uint64_t t0) {
     __builtin_amdgcn_s_sleep(16);
   }
   {
+    // The engine's status word is taken (read and cleared in one atomic, so
+    // that no flag set meanwhile is lost) along with the first loads.
+    uint32_t st = 0;
+    if (lane == 0) st = __hip_atomic_exchange(a.status, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    // Two ways to cover the chunks.  One lane per chunk, 64 chunks a pass,
+    // waits for P + 1 rounds of loads a pass (the mark stripes, then each
+    // receiver's row).  One (chunk, receiver) row per lane, 64 / P chunks a
+    // pass, issues all of a lane's loads under one wait, but a pass costs
+    // about two such rounds (more loads, the combining shuffles): the wave
+    // takes the way with fewer rounds (8 ranks' whole() round: 6.4 us -> 3.1;
+    // 40 chunks of 8 ranks: 5.4 us one lane per chunk, 6.9 us by rows).
     const CheckView v{a.chunks, a.gates, a.gate_stride, a.marks, a.nranks, a.round};
-    for (uint32_t g = lane; g < a.nchunks; g += 64)
-      __hip_atomic_store(a.chk_flags + g, check_chunk(v, g), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_SYSTEM);
-    const uint32_t st = wave_load_sys(a.status);
-    if (lane == 0) {
-      __hip_atomic_store(a.chk_status, st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      __hip_atomic_store(a.status, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const uint32_t P = a.nranks, per = 64 / P, nb = 64 / per, B = per * nb;
+    const uint32_t row_passes = (a.nchunks + per - 1) / per;
+    const uint32_t chunk_rounds = (a.nchunks + 63) / 64 * (P + 1);
+    if (2 * row_passes > chunk_rounds) {
+      for (uint32_t g = lane; g < a.nchunks; g += 64)
+        __hip_atomic_store(a.chk_flags + g, check_chunk(v, g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    } else {
+      // By rows: every lane also sums its chunk's mark stripes (the chunk's
+      // first lane's sum is used), so no load sits under a lane condition;
+      // idle lanes load chunk G-1's words and drop them.  A chunk's lanes
+      // are combined in its first lane, and each pass's results move to the
+      // lane of their chunk in a batch of up to 64, stored together: the
+      // stores go to host memory, and a store per pass would put its round
+      // trip in front of the next pass's loads.
+      const uint32_t lg = lane / P, q = lane - lg * P;
+      for (uint32_t b0 = 0; b0 < a.nchunks; b0 += B) {
+        uint32_t acc = 0;
+        for (uint32_t k = 0; k < nb && b0 + k * per < a.nchunks; ++k) {
+          const uint32_t g = b0 + k * per + lg;
+          const bool mine = lg < per && g < a.nchunks;
+          const uint32_t gl = mine ? g : a.nchunks - 1;
+          const RowWords w = load_row(v, gl, q);
+          const uint64_t marks = load_marks(v, gl);
+          const ChunkD& cd = a.chunks[gl];
+          const uint32_t rank = cd.rank, writers = cd.writers;
+          uint32_t f = judge_row(w, q == rank, a.round) | (q == 0 ? judge_marks(marks, writers, a.round) : 0u);
+          f = mine ? f : 0u;
+          uint32_t all = f;  // valid in each chunk's first lane
+          for (uint32_t j = 1; j < P; ++j) all |= (uint32_t)__shfl((int)f, (int)(lane + j));
+          const uint32_t t = lane - k * per;  // wraps below this pass's lanes
+          const uint32_t got = (uint32_t)__shfl((int)all, (int)(t * P));
+          acc = t < per ? got : acc;
+        }
+        if (lane < B && b0 + lane < a.nchunks)
+          __hip_atomic_store(a.chk_flags + b0 + lane, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
     }
+    if (lane == 0) __hip_atomic_store(a.chk_status, st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     wave_wait_stores();
     if (lane == 0)
       __hip_atomic_store(a.chk_seq_host, a.chk_seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -656,9 +716,8 @@ __global__ __launch_bounds__(kCheckThreads) void check_kernel(CheckArgs a) {
   for (uint32_t g = threadIdx.x; g < a.G; g += kCheckThreads)
     __hip_atomic_store(a.flags + g, check_chunk(a.v, g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   if (threadIdx.x == 0) {
-    const uint32_t st = __hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const uint32_t st = __hip_atomic_exchange(a.status, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     __hip_atomic_store(a.status_host, st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    __hip_atomic_store(a.status, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
   __syncthreads();
   if (threadIdx.x == 0)
@@ -1441,6 +1500,7 @@ int tc_plan_wait(tc_plan* P, uint64_t timeout_us) {
     in_engine = engine_check_by(P, deadline);
   }
   P->engine_chk_seq = 0;
+  P->checked_in_engine = in_engine == 1;
   bool timed_out = false;
   if (in_engine != 1) {
     if (int rc = queue_check(P)) return rc;
@@ -1728,6 +1788,7 @@ int tc_plan_stats(tc_plan* P, tc_stats* out) {
   out->bytes_read = P->bytes_read;
   out->pieces = P->pieces.size();
   out->G = P->G;
+  out->engine_checked = P->checked_in_engine ? 1u : 0u;
   if (P->launch_seq) {
     uint32_t st[2] = {0, 0};
     const uint8_t* blk = P->ws + P->L.launch[P->cur_launch_block];

@@ -85,6 +85,7 @@ struct tc_plan {
   uint32_t* exit_dev = nullptr;
   uint32_t check_seq = 0;                   // last sequence number handed out
   uint32_t engine_chk_seq = 0;              // the running launch's check number (0: none)
+  bool checked_in_engine = false;           // the last wait()'s check ran in the engine
   bool check_queued = false;                // a check kernel was ever queued (ev_check_done)
   bool noalloc = false;                     // workspace = the device's static array
   std::vector<uint32_t> flags_buf;          // no-allocation plan: the check's flags, copied back
