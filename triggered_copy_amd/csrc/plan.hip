@@ -465,8 +465,8 @@ struct CheckArgs {
 
 constexpr int kCheckThreads = 1024;
 // Plans of up to this many chunks have their completion check run by the
-// engine's publisher (one wave, 64 / P chunks at a time); larger ones by the
-// check kernel.
+// engine's publisher (one wave, by chunks or by gate rows, see engine_check);
+// larger ones by the check kernel.
 constexpr uint32_t kEngineCheckMaxChunks = 256;
 
 // The sum of global chunk g's mark stripes, per lane (each lane its own g).
