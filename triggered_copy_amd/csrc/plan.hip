@@ -558,6 +558,7 @@ __device__ void engine_check(const EngineArgs& a, uint64_t t0) {
     // takes the way with fewer rounds (8 ranks' whole() round: 6.4 us -> 3.1;
     // 40 chunks of 8 ranks: 5.4 us one lane per chunk, 6.9 us by rows).
     const CheckView v{a.chunks, a.gates, a.gate_stride, a.marks, a.nranks, a.round};
+    static_assert(TC_MAX_RANKS <= 64, "a pass by rows holds every receiver of a chunk in one wave");
     const uint32_t P = a.nranks, per = 64 / P, nb = 64 / per, B = per * nb;
     const uint32_t row_passes = (a.nchunks + per - 1) / per;
     const uint32_t chunk_rounds = (a.nchunks + 63) / 64 * (P + 1);
