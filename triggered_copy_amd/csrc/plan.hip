@@ -720,6 +720,12 @@ __global__ __launch_bounds__(kCheckThreads) void check_kernel(CheckArgs a) {
     const uint32_t st = __hip_atomic_exchange(a.status, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     __hip_atomic_store(a.status_host, st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
+  // Every wave waits for its own flag stores (written through to host
+  // memory) before the barrier: thread 0's release of the sequence word
+  // waits only for its own wave's stores, and the barrier does not wait for
+  // stores, so without this the host could see the sequence word before
+  // another wave's flags.
+  wave_wait_stores();
   __syncthreads();
   if (threadIdx.x == 0)
     __hip_atomic_store(a.seq_host, a.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
